@@ -1,0 +1,5 @@
+"""Reproducible fused causal (grouped-query) attention for MI355X (gfx950).
+
+The compute path is the HIP library ``libattn.so`` behind the C ABI declared
+in ``include/attn.h``; this package only marshals torch tensors into it.
+"""
