@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Throughput of the fused causal GQA attention path (forward + backward) on one MI355X.
+
+One *step* is one pass of the whole hot path over one batch of synthetic input:
+attn_fwd, then the three backward steps attn_bwd_preprocess, attn_bwd_dkdv and
+attn_bwd_dq (the kernels attn_bwd runs), on the stream torch treats as current.
+The default workload is one layer of the 101.7M decoder of "Training a 100M
+transformer in pure Rust: RustingBrain vs PyTorch and TensorFlow" (section
+"The setup": GQA 12/4, head_dim 64) at the 4 x 1024 batch shape.
+
+Timing protocol: the correctness gate runs first (finite outputs, bitwise-equal
+hashes over repeated runs, exact-math invariants of the gradients), then
+``--warmup`` untimed steps, then exactly ``--steps`` steps between two device
+synchronisations, with a HIP event around every kernel launch so each kernel's
+average duration is measured in the same region.  ``value`` is algorithmic
+TFLOP/s (4*D forward + 10*D backward flops per unmasked (query, key) pair and
+query head) over the wall-clock time of the timed steps, inputs resident in HBM.
+
+The cpu_baseline leg times the fp64 numpy oracle on a bounded sample of
+(batch, KV-group) units of the same workload on the host cores, and compares
+its outputs with the GPU's on those units.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 bf16 flop/clk/CU (dense MFMA) x 2.4 GHz
+PEAK_HBM_GBS = 8000.0      # HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_digest() -> str:
+    """SHA-256 over the HIP sources and the header: identifies the kernels profiled."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "reproducible_causal_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "attn.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if current."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload, {}).get(kernel)
+    if not rec or rec.get("sources_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa-4x1024")
+    ap.add_argument("--layers", type=int, default=16,
+                    help="also time a stack of this many independent layers (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle cpu_baseline sample (0: skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: the attention path has no cross-GPU step and "
+              "this build runs on a single GPU; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from reproducible_causal_attention_amd import attn as A
+    from reproducible_causal_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    lib = A.load_library()
+    w = W.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench.py times bf16 workloads", file=sys.stderr)
+        return 2
+    B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
+    dev = torch.device("cuda:0")
+    log("workload", w.name, w.label(), "|", lib.attn_build_info().decode())
+
+    inp = W.generate(w)
+    q, k, v, dO = (torch.from_numpy(getattr(inp, n).view(np.int16)).view(torch.bfloat16).to(dev)
+                   for n in ("q", "k", "v", "dO"))
+
+    def buffers():
+        return dict(o=torch.empty_like(q), lse=torch.empty((B, Hq, T), device=dev),
+                    delta=torch.empty((B, Hq, T), device=dev), dq=torch.empty_like(q),
+                    dk=torch.empty_like(k), dv=torch.empty_like(v))
+
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    bf = A.ATTN_BF16
+    causal = int(w.causal)
+
+    def launch(fn_name, *a):
+        st = getattr(lib, fn_name)(*a)
+        if st != 0:
+            raise RuntimeError(f"{fn_name}: {lib.attn_status_string(st).decode()}")
+
+    def step(x, bufs, events=None):
+        qq, kk, vv, dd = x
+        b = bufs
+        if events is not None:
+            events[0].record(stream)
+        launch("attn_fwd", qq.data_ptr(), kk.data_ptr(), vv.data_ptr(), b["o"].data_ptr(),
+               b["lse"].data_ptr(), B, T, Hq, Hkv, D, w.scale, causal, bf, s)
+        if events is not None:
+            events[1].record(stream)
+        launch("attn_bwd_preprocess", b["o"].data_ptr(), dd.data_ptr(), b["delta"].data_ptr(),
+               B, T, Hq, D, bf, s)
+        if events is not None:
+            events[2].record(stream)
+        launch("attn_bwd_dkdv", qq.data_ptr(), kk.data_ptr(), vv.data_ptr(), dd.data_ptr(),
+               b["lse"].data_ptr(), b["delta"].data_ptr(), b["dk"].data_ptr(), b["dv"].data_ptr(),
+               B, T, Hq, Hkv, D, w.scale, causal, bf, s)
+        if events is not None:
+            events[3].record(stream)
+        launch("attn_bwd_dq", qq.data_ptr(), kk.data_ptr(), vv.data_ptr(), dd.data_ptr(),
+               b["lse"].data_ptr(), b["delta"].data_ptr(), b["dq"].data_ptr(),
+               B, T, Hq, Hkv, D, w.scale, causal, bf, s)
+        if events is not None:
+            events[4].record(stream)
+
+    def digest(b):
+        h = hashlib.sha256()
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            h.update(b[n].contiguous().view(torch.uint8).cpu().numpy().tobytes())
+        return h.hexdigest()
+
+    # ---- correctness gate (no oracle): finite, reproducible, invariants ----
+    bufs = buffers()
+    hashes = []
+    for _ in range(3):
+        step((q, k, v, dO), bufs)
+        torch.cuda.synchronize()
+        hashes.append(digest(bufs))
+    gate = {"finite": all(bool(torch.isfinite(bufs[n].float()).all()) for n in bufs),
+            "hash_repeats_equal": len(set(hashes)) == 1}
+    G = Hq // Hkv
+    dv32, dk32, dO32 = bufs["dv"].float(), bufs["dk"].float(), dO.float()
+    # Rows of P sum to one: sum_j dv_j equals the sum of dO over the group's query rows.
+    want = dO32.view(B, T, Hkv, G, D).sum(dim=(1, 3))
+    got = dv32.sum(dim=1)
+    gate["dv_column_sum_rel_err"] = float((got - want).abs().max() / want.abs().max())
+    # Key-translation invariance: sum_j dk_j = 0, relative to the column sums of |dk|.
+    gate["dk_sum_rel"] = float(dk32.sum(dim=1).abs().max() / dk32.abs().sum(dim=1).max())
+    gate["ok"] = (gate["finite"] and gate["hash_repeats_equal"]
+                  and gate["dv_column_sum_rel_err"] < 2e-2 and gate["dk_sum_rel"] < 2e-2)
+    log("gate", gate)
+    if not gate["ok"]:
+        print(json.dumps({"metric": "gate failed", "gate": gate}), flush=True)
+        return 1
+
+    # ---- timed region ----
+    for _ in range(args.warmup):
+        step((q, k, v, dO), bufs)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step((q, k, v, dO), bufs, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+    per_kernel_us = {n: 1e3 * float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+                     for j, n in enumerate(names)}
+    event_step_us = 1e3 * float(np.mean([e[0].elapsed_time(e[4]) for e in evs]))
+    ms_per_step = 1e3 * wall / args.steps
+    flops = w.fwd_flops + w.bwd_flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"step {ms_per_step * 1e3:.1f} us wall, {event_step_us:.1f} us by events; "
+        f"{tflops:.1f} TFLOP/s; kernels {per_kernel_us}")
+
+    # ---- roofline of the dominant kernel ----
+    pairs = w.causal_pairs
+    algo = {  # algorithmic work of one launch (flops, or bytes for the preprocess)
+        "fwd": 4.0 * D * pairs,
+        "bwd_dkdv": 8.0 * D * pairs,   # S, dP, dV, dK
+        "bwd_dq": 6.0 * D * pairs,     # S and dP recomputed, dQ
+        "bwd_preprocess": 2.0 * B * T * Hq * D * 2 + 4.0 * B * Hq * T,
+    }
+    dom = max(per_kernel_us, key=per_kernel_us.get)
+    sec = per_kernel_us[dom] * 1e-6
+    src_digest = kernel_sources_digest()
+    traffic = load_traffic(dom, w.name, src_digest)
+    if dom == "bwd_preprocess":
+        achieved = algo[dom] / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = algo[dom] / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = round(per_kernel_us[dom], 2)
+    pre_gbs = algo["bwd_preprocess"] / (per_kernel_us["bwd_preprocess"] * 1e-6) / 1e9
+
+    # ---- a stack of independent layers (forward 0..L-1, backward L-1..0) ----
+    layers = None
+    if args.layers > 0:
+        L = args.layers
+        xs = [(torch.randn_like(q, dtype=torch.float32).to(torch.bfloat16),
+               torch.randn_like(k, dtype=torch.float32).to(torch.bfloat16),
+               torch.randn_like(v, dtype=torch.float32).to(torch.bfloat16),
+               torch.randn_like(dO, dtype=torch.float32).to(torch.bfloat16)) for _ in range(L)]
+        bs = [buffers() for _ in range(L)]
+
+        def stack_step():
+            for i in range(L):
+                x, b = xs[i], bs[i]
+                launch("attn_fwd", x[0].data_ptr(), x[1].data_ptr(), x[2].data_ptr(),
+                       b["o"].data_ptr(), b["lse"].data_ptr(), B, T, Hq, Hkv, D, w.scale,
+                       causal, bf, s)
+            for i in reversed(range(L)):
+                x, b = xs[i], bs[i]
+                launch("attn_bwd_preprocess", b["o"].data_ptr(), x[3].data_ptr(),
+                       b["delta"].data_ptr(), B, T, Hq, D, bf, s)
+                launch("attn_bwd_dkdv", x[0].data_ptr(), x[1].data_ptr(), x[2].data_ptr(),
+                       x[3].data_ptr(), b["lse"].data_ptr(), b["delta"].data_ptr(),
+                       b["dk"].data_ptr(), b["dv"].data_ptr(), B, T, Hq, Hkv, D, w.scale,
+                       causal, bf, s)
+                launch("attn_bwd_dq", x[0].data_ptr(), x[1].data_ptr(), x[2].data_ptr(),
+                       x[3].data_ptr(), b["lse"].data_ptr(), b["delta"].data_ptr(),
+                       b["dq"].data_ptr(), B, T, Hq, Hkv, D, w.scale, causal, bf, s)
+
+        for _ in range(3):
+            stack_step()
+        n_stack = max(3, args.steps // L)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_stack):
+            stack_step()
+        torch.cuda.synchronize()
+        st = (time.perf_counter() - t0) / n_stack
+        layers = {"layers": L, "steps": n_stack, "ms_per_step": round(st * 1e3, 4),
+                  "tflops": round(L * flops / st / 1e12, 1),
+                  "pct_peak": round(100 * L * flops / st / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        log("layer stack", layers)
+        del xs, bs
+
+    # ---- cpu_baseline: the oracle on a bounded sample of the same workload ----
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, inp, bufs, args.cpu_seconds)
+        log("cpu_baseline", cpu)
+
+    out = {
+        "metric": "attn fwd+bwd TFLOP/s & % bf16 MFMA peak, B4·T1024 GQA12/4 d64",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D,
+                   "causal": bool(w.causal), "scale": w.scale,
+                   "gflop_per_step": round(flops / 1e9, 4)},
+        "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "per_kernel_us": {n: round(u, 2) for n, u in per_kernel_us.items()},
+        "event_step_us": round(event_step_us, 2),
+        "preprocess_gbs": round(pre_gbs, 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layers": layers,
+        "gate": gate,
+        "output_sha256": hashes[0],
+        "sources_digest": src_digest,
+        "build": lib.attn_build_info().decode(),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+    if cpu is not None and not cpu.get("parity_ok", True):
+        return 1
+    return 0
+
+
+def cpu_baseline(w, inp, bufs, budget_s):
+    """Time the fp64 oracle on (batch, KV-group) units until ``budget_s`` is spent,
+    and compare the GPU outputs of those units with it."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing or unusable
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    q, k, v, dO = (inp.as_float64(n) for n in ("q", "k", "v", "dO"))
+    gpu = {n: bufs[n].float().cpu().numpy().astype(np.float64) for n in ("o", "lse", "dq", "dk", "dv")}
+    units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    G = w.G
+    done, secs, worst = 0, 0.0, {}
+    for b, g in units:
+        t0 = time.perf_counter()
+        o_r, lse_r = oracle.ref_fwd_group(q, k, v, w.scale, w.causal, b, g)
+        dq_r, dk_r, dv_r, _ = oracle.ref_bwd_group(q, k, v, dO, w.scale, w.causal, b, g)
+        secs += time.perf_counter() - t0
+        done += 1
+        hs = slice(g * G, (g + 1) * G)
+        pairs = (("o", gpu["o"][b, :, hs], o_r), ("dq", gpu["dq"][b, :, hs], dq_r),
+                 ("dk", gpu["dk"][b, :, g], dk_r), ("dv", gpu["dv"][b, :, g], dv_r))
+        for n, a, r in pairs:
+            worst[n] = max(worst.get(n, 0.0), float(np.max(np.abs(a - r)) / np.max(np.abs(r))))
+        worst["lse"] = max(worst.get("lse", 0.0), float(np.max(np.abs(gpu["lse"][b, hs] - lse_r))))
+        if secs >= budget_s:
+            break
+    pairs_per_unit = G * (w.T * (w.T + 1) // 2 if w.causal else w.T * w.T)
+    flops = done * pairs_per_unit * (4.0 + 10.0) * w.D
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {len(units)} (batch, KV-group) units of {w.name}, fwd+bwd, "
+                      f"{secs:.2f} s",
+            "seconds": round(secs, 3),
+            "max_err_vs_gpu": {n: float(f"{e:.3g}") for n, e in worst.items()},
+            "parity_ok": all(e <= 2e-2 for e in worst.values())}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

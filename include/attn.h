@@ -1,0 +1,142 @@
+/*
+ * attn.h -- C ABI of the reproducible fused causal attention library (libattn.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is causal (optionally grouped-query) scaled-dot-product
+ * attention for decoder training, forward and backward, computed without ever
+ * materialising the [T, T] score matrix.  "Training a 100M transformer in pure
+ * Rust: RustingBrain vs PyTorch and TensorFlow" motivates it: section "Step 1:
+ * measure before changing anything" finds the cost of unfused attention in the
+ * [seq_len, seq_len] fp32 matrix written and read back by causal_softmax_lse,
+ * causal_softmax_bwd and causal_probs_from_lse; section "Step 2: fused flash
+ * attention" removes the matrix with one fused forward and backward.  Section
+ * "The setup" gives the grouped-query shape (12 query heads, 4 KV heads,
+ * head_dim 64).
+ *
+ * Definitions (per batch element b, query head h, KV head g = h / (Hq/Hkv)):
+ *   s[i][j]  = scale * sum_d q[b][i][h][d] * k[b][j][g][d]; with causal=1 key j
+ *              is visible to query i iff j <= i, otherwise s = -inf;
+ *   lse[i]   = ln(sum_j exp(s[i][j]))                        (natural log)
+ *   P[i][j]  = exp(s[i][j] - lse[i]);   o[b][i][h][:] = sum_j P[i][j] v[b][j][g][:]
+ *   delta[i] = sum_d dO[b][i][h][d] * o[b][i][h][d]
+ *   dS[i][j] = P[i][j] * (sum_d dO[b][i][h][d] * v[b][j][g][d] - delta[i])
+ *   dq[i] = scale * sum_j dS[i][j] k[j];  dk[j] = scale * sum_{h in group} sum_i dS[i][j] q[i];
+ *   dv[j] = sum_{h in group} sum_i P[i][j] dO[i].
+ *
+ * Layouts (all row-major and contiguous; there are no stride arguments):
+ *   q, o, dO, dq : [B, T, Hq,  D] elements of the input dtype
+ *   k, v, dk, dv : [B, T, Hkv, D] elements of the input dtype
+ *   lse, delta   : [B, Hq, T]     float32
+ *
+ * Ownership and execution.  Every pointer is caller-owned device memory on the
+ * current HIP device.  The library allocates nothing, keeps no mutable global
+ * state and is safe to call from several host threads.  Calls enqueue work on
+ * `stream` (a hipStream_t; NULL is the null stream) and return without
+ * waiting for it.  Outputs are overwritten, never accumulated into, so callers
+ * need not clear them first.
+ *
+ * Reproducibility.  For one build of the library on one device, identical
+ * inputs give bitwise-identical outputs, whatever the stream, the launch order
+ * or concurrent work: every reduction runs in a fixed order inside one
+ * workgroup and no kernel uses atomics.  ("rust-trainer", section "The trainer
+ * is not bit-identical to itself after step 1", traces the loss of bit
+ * identity to a gradient accumulated with atomics.)  Bits are not promised
+ * across builds, tile constants or GPU models.
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued; a
+ * failed validation enqueues nothing.  ATTN_ERR_INVALID_ARG: a null pointer; a
+ * size <= 0; Hq not a multiple of Hkv; causal not 0 or 1; scale not finite; a
+ * pointer not 16-byte aligned; an output range overlapping an input range or
+ * another output; a workspace smaller than attn_bwd_workspace_bytes(); sizes
+ * beyond the limits below.  ATTN_ERR_UNSUPPORTED: D != 64 or an unknown dtype.
+ * ATTN_ERR_HIP: the HIP runtime reported an error for a launch (the value of
+ * hipGetLastError() after the launch).  Nothing aborts and no C++ exception
+ * crosses the interface.
+ *
+ * Limits: T <= 2^24, B*Hq <= 2^20, and every tensor holds fewer than 2^40
+ * elements.
+ */
+#ifndef REPRODUCIBLE_CAUSAL_ATTENTION_ATTN_H
+#define REPRODUCIBLE_CAUSAL_ATTENTION_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,
+  ATTN_ERR_UNSUPPORTED = 2,
+  ATTN_ERR_HIP = 3
+} attn_status_t;
+
+typedef enum {
+  ATTN_F32 = 0,  /* float32 inputs and outputs, float32 arithmetic throughout   */
+  ATTN_BF16 = 1  /* bfloat16 inputs and outputs; bf16 matrix products with fp32
+                    accumulation, fp32 softmax statistics, lse and delta        */
+} attn_dtype_t;
+
+/* Forward.  Reads q, k, v; writes o and lse (the per-row log-sum-exp that the
+ * backward uses to recompute P, as causal_probs_from_lse does in "Training a
+ * 100M transformer in pure Rust: RustingBrain vs PyTorch and TensorFlow",
+ * section "Step 1: measure before changing anything").  o and lse must not
+ * overlap the inputs or each other. */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                       attn_dtype_t dtype, void* stream);
+
+/* Bytes of device workspace attn_bwd needs: the float32 delta rows
+ * (B*Hq*T*4 bytes) rounded up to 256 bytes.  Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype);
+
+/* Backward of sum(o * dO).  o and lse must be the outputs of attn_fwd for the
+ * same q, k, v, scale and causal.  Enqueues, in order, attn_bwd_preprocess
+ * (delta into the workspace), attn_bwd_dkdv and attn_bwd_dq.  dq, dk, dv must
+ * not overlap any input, the workspace or each other; the workspace must hold
+ * at least attn_bwd_workspace_bytes() bytes and is clobbered. */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                       int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Backward step 1: delta[b][h][i] = sum_d dO[b][i][h][d] * o[b][i][h][d], accumulated
+ * in float32 (the row term of the softmax backward that causal_softmax_bwd needs
+ * in the unfused chain of the same page, section "Step 1").  o and dO are
+ * [B, T, Hq, D]; delta is [B, Hq, T] float32 and must not overlap them. */
+attn_status_t attn_bwd_preprocess(const void* o, const void* dO, float* delta,
+                                  int B, int T, int Hq, int D, attn_dtype_t dtype,
+                                  void* stream);
+
+/* Backward step 2: dk and dv.  One workgroup owns a tile of keys of one KV head
+ * and visits every query head of its group and every query tile that can see
+ * those keys, in a fixed order, so dk and dv are summed in registers and written
+ * once, with no atomics.  delta is the output of attn_bwd_preprocess. */
+attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                            const float* lse, const float* delta, void* dk, void* dv,
+                            int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                            attn_dtype_t dtype, void* stream);
+
+/* Backward step 3: dq.  One workgroup owns a tile of queries of one query head
+ * and visits the key tiles it can see in a fixed order. */
+attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                          const float* lse, const float* delta, void* dq,
+                          int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                          attn_dtype_t dtype, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_string(attn_status_t status);
+
+/* Static string describing this build: source revision, offload architecture,
+ * compiler and tile constants.  Output bits are promised identical only
+ * between runs of the same build ("rust-trainer", section "Build once, run
+ * many", prints the resolved revision of every binary it measures). */
+const char* attn_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPRODUCIBLE_CAUSAL_ATTENTION_ATTN_H */

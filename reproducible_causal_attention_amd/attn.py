@@ -1,0 +1,175 @@
+"""ctypes binding of libattn.so (include/attn.h) for torch tensors.
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels of the library.  torch supplies device memory (``torch.empty``) and the
+stream (``torch.cuda.current_stream()``).  If the library is missing the calls
+raise; there is no fallback.
+
+Layouts: q, o, dO, dq are [B, T, Hq, 64]; k, v, dk, dv are [B, T, Hkv, 64]
+(contiguous, bfloat16 or float32); lse and delta are [B, Hq, T] float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+from . import build as _build
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16 = 0, 1
+
+EXPORTED = (
+    "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+    "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string", "attn_build_info",
+)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libattn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m reproducible_causal_attention_amd.build` "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    sizes = [I, I, I, I, I]
+    lib.attn_fwd.argtypes = [P, P, P, P, P, *sizes, F, I, I, P]
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, *sizes, F, I, I, P, Z, P]
+    lib.attn_bwd_workspace_bytes.argtypes = [*sizes, I]
+    lib.attn_bwd_workspace_bytes.restype = Z
+    lib.attn_bwd_preprocess.argtypes = [P, P, P, I, I, I, I, I, P]
+    lib.attn_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, P, *sizes, F, I, I, P]
+    lib.attn_bwd_dq.argtypes = [P, P, P, P, P, P, P, *sizes, F, I, I, P]
+    for name in ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"):
+        getattr(lib, name).restype = I
+    lib.attn_status_string.argtypes = [I]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_build_info.argtypes = []
+    lib.attn_build_info.restype = ctypes.c_char_p
+    if path == library_path():
+        _lib = lib
+    return lib
+
+
+def build_info() -> str:
+    return load_library().attn_build_info().decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = load_library()
+        raise AttnError(status, lib.attn_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t: torch.Tensor) -> int:
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _shapes(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, T, Hq, D] and k, v [B, T, Hkv, D]")
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    return B, T, Hq, Hkv, D
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def fwd(q, k, v, scale=None, causal=True):
+    """Forward: returns ``(o [B,T,Hq,D], lse [B,Hq,T] float32)``."""
+    lib = load_library()
+    B, T, Hq, Hkv, D = _shapes(q, k)
+    scale = default_scale(D) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D,
+                        scale, int(bool(causal)), _dtype_code(q), _stream()))
+    return o, lse
+
+
+def workspace_bytes(B, T, Hq, Hkv, D, dtype_code) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype_code))
+
+
+def bwd(q, k, v, o, lse, dO, scale=None, causal=True, workspace=None):
+    """Backward of sum(o * dO): returns ``(dq, dk, dv)``."""
+    lib = load_library()
+    B, T, Hq, Hkv, D = _shapes(q, k)
+    scale = default_scale(D) if scale is None else float(scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = workspace_bytes(B, T, Hq, Hkv, D, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                        _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale, int(bool(causal)),
+                        _dtype_code(q), _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+def bwd_preprocess(o, dO):
+    """delta = rowsum(dO * o) as [B, Hq, T] float32."""
+    lib = load_library()
+    B, T, Hq, D = o.shape
+    delta = torch.empty((B, Hq, T), dtype=torch.float32, device=o.device)
+    _check(lib.attn_bwd_preprocess(_ptr(o), _ptr(dO), _ptr(delta), B, T, Hq, D,
+                                   _dtype_code(o), _stream()))
+    return delta
+
+
+def bwd_dkdv(q, k, v, dO, lse, delta, scale=None, causal=True):
+    lib = load_library()
+    B, T, Hq, Hkv, D = _shapes(q, k)
+    scale = default_scale(D) if scale is None else float(scale)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    _check(lib.attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
+                             _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale, int(bool(causal)),
+                             _dtype_code(q), _stream()))
+    return dk, dv
+
+
+def bwd_dq(q, k, v, dO, lse, delta, scale=None, causal=True):
+    lib = load_library()
+    B, T, Hq, Hkv, D = _shapes(q, k)
+    scale = default_scale(D) if scale is None else float(scale)
+    dq = torch.empty_like(q)
+    _check(lib.attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
+                           _ptr(dq), B, T, Hq, Hkv, D, scale, int(bool(causal)),
+                           _dtype_code(q), _stream()))
+    return dq

@@ -1,0 +1,221 @@
+// attn_api.hip -- the exported C ABI (include/attn.h): host-side validation,
+// workspace sizing and kernel launches.  Validation runs entirely on the host
+// and touches no HIP API, so every error path can be exercised without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/attn.h"
+#include "launch.hpp"
+
+#define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+#ifndef ATTN_GIT_REV
+#define ATTN_GIT_REV "unknown"
+#endif
+
+namespace {
+
+constexpr long long kMaxT = 1LL << 24;
+constexpr long long kMaxTiles = 1LL << 23;     // ceil(T/64) * B * Hq
+constexpr long long kMaxElements = 1LL << 40;  // per tensor
+
+struct Span {
+  uintptr_t lo, hi;
+};
+
+Span span_of(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Span{lo, lo + bytes};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(attn_dtype_t dt) { return dt == ATTN_F32 ? 4 : 2; }
+
+// Sizes and dtype, shared by every entry point (Hkv = Hq where no KV tensor is involved).
+attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (T > kMaxT) return ATTN_ERR_INVALID_ARG;
+  const long long tiles = ((long long)T + 63) / 64 * (long long)B * (long long)Hq;
+  if (tiles >= kMaxTiles) return ATTN_ERR_INVALID_ARG;
+  if ((long long)B * T * Hq * (long long)D >= kMaxElements) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (D != rca::kHeadDim) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status_t check_scalars(float scale, int causal) {
+  if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+// Null and alignment checks over a list of pointers.
+attn_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs) {
+    if (p == nullptr || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
+// No output may overlap an input or another output.
+attn_status_t check_disjoint(std::initializer_list<Span> inputs, std::initializer_list<Span> outputs) {
+  for (auto o = outputs.begin(); o != outputs.end(); ++o) {
+    for (const Span& i : inputs)
+      if (overlap(*o, i)) return ATTN_ERR_INVALID_ARG;
+    for (auto o2 = o + 1; o2 != outputs.end(); ++o2)
+      if (overlap(*o, *o2)) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
+rca::Problem make_problem(int B, int T, int Hq, int Hkv, float scale, int causal) {
+  rca::Problem p;
+  p.B = B;
+  p.T = T;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.causal = causal;
+  return p;
+}
+
+attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+#define ATTN_TRY(expr)                       \
+  do {                                       \
+    const attn_status_t st_ = (expr);        \
+    if (st_ != ATTN_OK) return st_;          \
+  } while (0)
+
+}  // namespace
+
+ATTN_EXPORT attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                                   attn_dtype_t dtype, void* stream) {
+  ATTN_TRY(check_ptrs({q, k, v, o, lse}));
+  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_scalars(scale, causal));
+  const size_t es = elem_size(dtype);
+  const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
+  const size_t lb = (size_t)B * Hq * T * sizeof(float);
+  ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb)},
+                          {span_of(o, qb), span_of(lse, lb)}));
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(dtype == ATTN_BF16 ? rca::launch_fwd_bf16(p, q, k, v, o, lse, s)
+                                     : rca::launch_fwd_f32(p, q, k, v, o, lse, s));
+}
+
+ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype) {
+  if (check_shape(B, T, Hq, Hkv, D, dtype) != ATTN_OK) return 0;
+  const size_t bytes = (size_t)B * Hq * T * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+ATTN_EXPORT attn_status_t attn_bwd_preprocess(const void* o, const void* dO, float* delta, int B,
+                                              int T, int Hq, int D, attn_dtype_t dtype,
+                                              void* stream) {
+  ATTN_TRY(check_ptrs({o, dO, delta}));
+  ATTN_TRY(check_shape(B, T, Hq, Hq, D, dtype));
+  const size_t qb = (size_t)B * T * Hq * D * elem_size(dtype);
+  const size_t lb = (size_t)B * Hq * T * sizeof(float);
+  ATTN_TRY(check_disjoint({span_of(o, qb), span_of(dO, qb)}, {span_of(delta, lb)}));
+  const rca::Problem p = make_problem(B, T, Hq, Hq, 1.0f, 1);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(dtype == ATTN_BF16 ? rca::launch_bwd_pre_bf16(p, o, dO, delta, s)
+                                     : rca::launch_bwd_pre_f32(p, o, dO, delta, s));
+}
+
+ATTN_EXPORT attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                                        const float* lse, const float* delta, void* dk, void* dv,
+                                        int B, int T, int Hq, int Hkv, int D, float scale,
+                                        int causal, attn_dtype_t dtype, void* stream) {
+  ATTN_TRY(check_ptrs({q, k, v, dO, lse, delta, dk, dv}));
+  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_scalars(scale, causal));
+  const size_t es = elem_size(dtype);
+  const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
+  const size_t lb = (size_t)B * Hq * T * sizeof(float);
+  ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(dO, qb),
+                           span_of(lse, lb), span_of(delta, lb)},
+                          {span_of(dk, kb), span_of(dv, kb)}));
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(dtype == ATTN_BF16
+                      ? rca::launch_bwd_dkdv_bf16(p, q, k, v, dO, lse, delta, dk, dv, s)
+                      : rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s));
+}
+
+ATTN_EXPORT attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                                      const float* lse, const float* delta, void* dq, int B, int T,
+                                      int Hq, int Hkv, int D, float scale, int causal,
+                                      attn_dtype_t dtype, void* stream) {
+  ATTN_TRY(check_ptrs({q, k, v, dO, lse, delta, dq}));
+  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_scalars(scale, causal));
+  const size_t es = elem_size(dtype);
+  const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
+  const size_t lb = (size_t)B * Hq * T * sizeof(float);
+  ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(dO, qb),
+                           span_of(lse, lb), span_of(delta, lb)},
+                          {span_of(dq, qb)}));
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(dtype == ATTN_BF16 ? rca::launch_bwd_dq_bf16(p, q, k, v, dO, lse, delta, dq, s)
+                                     : rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
+}
+
+ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                                   int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                                   attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  ATTN_TRY(check_ptrs({q, k, v, o, lse, dO, dq, dk, dv, workspace}));
+  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_scalars(scale, causal));
+  const size_t need = attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype);
+  if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
+  const size_t lb = (size_t)B * Hq * T * sizeof(float);
+  ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(o, qb),
+                           span_of(lse, lb), span_of(dO, qb)},
+                          {span_of(dq, qb), span_of(dk, kb), span_of(dv, kb),
+                           span_of(workspace, need)}));
+  float* delta = static_cast<float*>(workspace);
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16) {
+    ATTN_TRY(from_hip(rca::launch_bwd_pre_bf16(p, o, dO, delta, s)));
+    ATTN_TRY(from_hip(rca::launch_bwd_dkdv_bf16(p, q, k, v, dO, lse, delta, dk, dv, s)));
+    return from_hip(rca::launch_bwd_dq_bf16(p, q, k, v, dO, lse, delta, dq, s));
+  }
+  ATTN_TRY(from_hip(rca::launch_bwd_pre_f32(p, o, dO, delta, s)));
+  ATTN_TRY(from_hip(rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s)));
+  return from_hip(rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
+}
+
+ATTN_EXPORT const char* attn_status_string(attn_status_t status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: unsupported head dimension or dtype";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown attn_status_t";
+}
+
+ATTN_EXPORT const char* attn_build_info(void) {
+  static const std::string info = std::string("revision=") + ATTN_GIT_REV +
+                                  " arch=gfx950 compiler=clang-" + __clang_version__ + " " +
+                                  rca::fwd_bf16_tiles() + " " + rca::bwd_bf16_tiles() + " " +
+                                  rca::f32_tiles();
+  return info.c_str();
+}

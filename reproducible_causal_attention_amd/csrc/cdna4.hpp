@@ -1,0 +1,131 @@
+// cdna4.hpp -- gfx950 building blocks shared by the attention kernels:
+// MFMA wrappers, bf16 packing, LDS transpose reads and cross-lane helpers.
+//
+// Register layouts of v_mfma_f32_32x32x16_bf16 (one 64-lane wave; g = lane / 32):
+//   A (32 x 16, M x K): lane holds row m = lane % 32, k = 8g + e for e = 0..7
+//   B (16 x 32, K x N): lane holds col n = lane % 32, k = 8g + e
+//   C (32 x 32):        lane holds col n = lane % 32 and rows
+//                       m = 8*(r/4) + 4g + (r%4) in its accumulator register r = 0..15
+// (measured on MI355X with random operands).  Because A and B use the same
+// (lane, e) -> k map, any permutation of the physical contraction index applied
+// to both operands leaves the product unchanged; the kernels use this to feed
+// an accumulator straight back as the next product's operand: accumulator
+// registers 8t..8t+7 of a 32-row block hold the 16 rows 16t + {8*(e/4) + 4g + e%4},
+// which is exactly an operand k-step whose element e is row 16t + 8*(e/4) + 4g + e%4.
+//
+// ds_read_b64_tr_b16 (measured): within each group of 16 lanes, let lane s
+// supply an address of four consecutive 16-bit elements R[s][0..3]; lane i then
+// receives R[4j + i/4][i % 4] as its element j.  If lane s addresses
+// row (base + s/4), column (c0 + 4*(s%4)) of a row-major tile, lane i receives
+// column c0 + i of rows base + 0..3: a column of the tile, i.e. a transposed read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rca {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D += A * B on the matrix cores, 8 bf16 per lane per operand, fp32 accumulate.
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Two floats -> one dword of two bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Eight consecutive accumulator registers r0..r0+7 -> one bf16 MFMA operand.
+__device__ __forceinline__ u32x4_t pack_operand(const f32x16_t& acc, int r0) {
+  u32x4_t o;
+  o[0] = pack_bf16x2(acc[r0 + 0], acc[r0 + 1]);
+  o[1] = pack_bf16x2(acc[r0 + 2], acc[r0 + 3]);
+  o[2] = pack_bf16x2(acc[r0 + 4], acc[r0 + 5]);
+  o[3] = pack_bf16x2(acc[r0 + 6], acc[r0 + 7]);
+  return o;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Reductions across the two 32-lane halves of a wave with one v_permlane32_swap.
+// swap(x, x) leaves lane i < 32 with {x[i], x[i + 32]} and lane i + 32 with
+// {x[i], x[i + 32]} as well, so both halves combine the same two values in the
+// same order and get bitwise-equal results.
+__device__ __forceinline__ float halves_max(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// 16-byte LDS load / store.
+__device__ __forceinline__ u32x4_t lds_load16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void lds_store16(uint16_t* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+// ds_read_b64_tr_b16 on an LDS address.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Operand of a 32x32x16 product whose contraction index runs along the rows of a
+// row-major LDS tile and whose M (or N) index runs along its columns: lane l gets
+// column c0 + l%32 of rows row0 + {4g + 0..3} (elements 0..3) and row0 + 8 + {4g + 0..3}
+// (elements 4..7), g = l/32 -- the element order of an accumulator fed back as an
+// operand (see the header comment).
+__device__ __forceinline__ u32x4_t lds_operand_T(const uint16_t* tile, int pitch, int row0, int c0,
+                                                 int lane) {
+  const int grp = lane >> 4;   // 16-lane group 0..3
+  const int s = lane & 15;     // lane within the group
+  const int row = row0 + 4 * (grp >> 1) + (s >> 2);
+  const int col = c0 + 16 * (grp & 1) + 4 * (s & 3);
+  const u32x2_t lo = lds_read_tr16(tile + row * pitch + col);
+  const u32x2_t hi = lds_read_tr16(tile + (row + 8) * pitch + col);
+  u32x4_t o;
+  o[0] = lo[0];
+  o[1] = lo[1];
+  o[2] = hi[0];
+  o[3] = hi[1];
+  return o;
+}
+
+__device__ __forceinline__ u32x4_t zero4u() {
+  u32x4_t z;
+  z[0] = z[1] = z[2] = z[3] = 0u;
+  return z;
+}
+
+__device__ __forceinline__ u32x4_t gload16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+}  // namespace rca

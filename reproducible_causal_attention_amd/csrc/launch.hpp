@@ -1,0 +1,46 @@
+// launch.hpp -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace rca {
+
+constexpr int kHeadDim = 64;
+
+// Everything a kernel launch needs; pointers are device pointers already
+// validated by the C ABI layer (contiguous, 16-byte aligned, non-overlapping).
+struct Problem {
+  int B, T, Hq, Hkv;
+  float scale;       // softmax scale applied to q.k
+  float scale_log2;  // scale * log2(e): scores are kept in base-2 units on the GPU
+  int causal;
+};
+
+hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                           float* lse, hipStream_t s);
+hipError_t launch_bwd_pre_bf16(const Problem& p, const void* o, const void* dO, float* delta,
+                               hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                const void* dO, const float* lse, const float* delta, void* dk,
+                                void* dv, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                              const void* dO, const float* lse, const float* delta, void* dq,
+                              hipStream_t s);
+
+hipError_t launch_fwd_f32(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                          float* lse, hipStream_t s);
+hipError_t launch_bwd_pre_f32(const Problem& p, const void* o, const void* dO, float* delta,
+                              hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const Problem& p, const void* q, const void* k, const void* v,
+                               const void* dO, const float* lse, const float* delta, void* dk,
+                               void* dv, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const Problem& p, const void* q, const void* k, const void* v,
+                             const void* dO, const float* lse, const float* delta, void* dq,
+                             hipStream_t s);
+
+// Tile constants of each kernel family, reported by attn_build_info().
+const char* fwd_bf16_tiles();
+const char* bwd_bf16_tiles();
+const char* f32_tiles();
+
+}  // namespace rca
