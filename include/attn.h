@@ -53,8 +53,9 @@
  * hipGetLastError() after the launch).  Nothing aborts and no C++ exception
  * crosses the interface.
  *
- * Limits: T <= 2^24, B*Hq <= 2^20, and every tensor holds fewer than 2^40
- * elements.
+ * Limits: T <= 2^24; ceil(T/64)*B*Hq < 2^23; every tensor holds fewer than
+ * 2^40 elements; and one batch element of q (T*Hq*D elements) spans fewer than
+ * 2^31 bytes at four bytes per element.
  */
 #ifndef REPRODUCIBLE_CAUSAL_ATTENTION_ATTN_H
 #define REPRODUCIBLE_CAUSAL_ATTENTION_ATTN_H

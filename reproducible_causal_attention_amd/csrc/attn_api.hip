@@ -20,6 +20,7 @@ namespace {
 constexpr long long kMaxT = 1LL << 24;
 constexpr long long kMaxTiles = 1LL << 23;     // ceil(T/64) * B * Hq
 constexpr long long kMaxElements = 1LL << 40;  // per tensor
+constexpr long long kMaxBatchBytes = 1LL << 31; // one batch element of any tensor (buffer offsets are 32-bit)
 
 struct Span {
   uintptr_t lo, hi;
@@ -44,6 +45,7 @@ attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dty
   const long long tiles = ((long long)T + 63) / 64 * (long long)B * (long long)Hq;
   if (tiles >= kMaxTiles) return ATTN_ERR_INVALID_ARG;
   if ((long long)B * T * Hq * (long long)D >= kMaxElements) return ATTN_ERR_INVALID_ARG;
+  if ((long long)T * Hq * (long long)D * 4 >= kMaxBatchBytes) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (D != rca::kHeadDim) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
@@ -215,7 +217,7 @@ ATTN_EXPORT const char* attn_status_string(attn_status_t status) {
 ATTN_EXPORT const char* attn_build_info(void) {
   static const std::string info = std::string("revision=") + ATTN_GIT_REV +
                                   " arch=gfx950 compiler=clang-" + __clang_version__ + " " +
-                                  rca::fwd_bf16_tiles() + " " + rca::bwd_bf16_tiles() + " " +
+                                  rca::fwd_bf16_tiles() + " " + rca::bwd_dkdv_tiles() + " " + rca::bwd_dq_tiles() + " " +
                                   rca::f32_tiles();
   return info.c_str();
 }

@@ -128,4 +128,55 @@ __device__ __forceinline__ u32x4_t zero4u() {
 
 __device__ __forceinline__ u32x4_t gload16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// Buffer descriptor over [base, base + bytes).  The hardware range check
+// (measured on gfx950, and it includes the scalar offset) makes loads past the
+// end return zero and drops stores past the end, so tail rows need no branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore_f32(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+}
+
+// Index of the calling wave within its workgroup, as a scalar (wave-uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Wait for all of this wave's outstanding global/buffer loads.  Issued once
+// after loads that precede a loop, so the loop's own prefetches are the only
+// loads in flight inside it and the compiler's waits cover just those.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait for this wave's outstanding LDS operations; also a compiler memory barrier.
+// Used between a wave's writes to its private LDS region and its own reads.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroups are dispatched to the 8 XCDs round-robin (block i runs on XCD i % 8),
+// and each XCD has its own L2.  Work is described as units (group gi, rank r):
+// units of one group read the same K/V and rank orders a group's units from
+// heaviest to lightest.  When the group count is a multiple of 8, the units of
+// group gi all run on XCD gi % 8, and every XCD still receives its units heaviest
+// rank first; otherwise units go out heaviest rank first across all groups.
+// A bijection from [0, NG*U) onto the units.
+__device__ __forceinline__ void decode_unit(int i, int NG, int& gi, int& r) {
+  if ((NG & 7) == 0) {
+    const int x = i & 7, slot = i >> 3, M = NG >> 3;
+    r = slot / M;
+    gi = x + 8 * (slot - r * M);
+  } else {
+    r = i / NG;
+    gi = i - r * NG;
+  }
+}
+
 }  // namespace rca

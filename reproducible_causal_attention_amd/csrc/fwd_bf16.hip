@@ -8,20 +8,24 @@
 // written instead, so the backward can recompute probabilities from it (that
 // page's causal_probs_from_lse).
 //
-// Work decomposition (MI355X-first, not the page's Ampere design):
-//   * one workgroup = 4 waves = 128 query rows of one (batch, query head);
-//     each wave owns 32 query rows for the whole kernel;
-//   * key/value tiles of 64 rows are staged row-major in LDS (pitch 72 bf16,
-//     so 16-byte column reads of 32 consecutive rows hit distinct banks);
+// Decomposition (MI355X-first, not the page's Ampere design):
+//   * a workgroup of 8 waves owns 128 query rows of one (batch, query head):
+//     four 32-row query blocks times two key halves;
+//   * key/value tiles of 64 rows are staged row-major in LDS (pitch 72 bf16, so
+//     16-byte column reads of 32 consecutive rows hit distinct banks) and
+//     double-buffered; wave (qb, kh) runs an online softmax over keys
+//     32*kh .. 32*kh+31 of every tile, so each K/V row in LDS feeds four waves;
 //   * the wave computes S^T = K Q^T (keys x queries) with 32x32x16 bf16 MFMA, so
 //     every lane holds one query's scores: the row max and row sum need a single
-//     half-wave exchange (v_permlane32_swap), and the O^T = V^T P^T product takes
-//     the probabilities straight from the accumulators (packed to bf16, round to
+//     half-wave exchange (v_permlane32_swap), and O^T += V^T P^T takes the
+//     probabilities straight from the accumulators (packed to bf16, round to
 //     nearest even) with V^T read from the row-major tile by ds_read_b64_tr_b16;
+//   * the output rescale is skipped when no row's running max moved;
 //   * scores are kept in base-2 units (scale * log2 e folded in) so every
 //     exponential is one v_exp_f32;
-//   * query tiles are issued heaviest first (the causal loop length grows with
-//     the tile index).
+//   * the two key halves' states (max, sum, O) are merged in a fixed order;
+//   * query tiles are issued heaviest first, and the tiles of one
+//     (batch, KV head) group run on one XCD so they share its L2.
 // Every reduction has a fixed order, so results are bitwise reproducible.
 #include "cdna4.hpp"
 #include "launch.hpp"
@@ -29,47 +33,58 @@
 namespace rca {
 namespace {
 
-constexpr int BM = 128;     // query rows per workgroup
-constexpr int BN = 64;      // key rows per LDS tile
-constexpr int PITCH = 72;   // LDS row pitch in bf16 elements (144 bytes)
-constexpr int NTHREADS = 256;
+constexpr int BM = 128;    // query rows per workgroup
+constexpr int BN = 64;     // key rows per LDS tile
+constexpr int PITCH = 72;  // LDS row pitch in bf16 elements (144 bytes)
+constexpr int NWAVES = 8;
+constexpr int NTHREADS = NWAVES * 64;
+constexpr int TILE = BN * PITCH;
+constexpr int PART_STRIDE = 36;  // floats per lane in the merge buffer (32 of O, m, l)
+static_assert(4 * 64 * PART_STRIDE * 4 <= 4 * TILE * 2, "merge buffer must fit");
 
 __global__ __launch_bounds__(NTHREADS) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv,
     float scale_log2, int causal) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int l32 = lane & 31;
   const int g = lane >> 5;
+  const int qb = wave & 3;
+  const int kh = wave >> 2;
 
+  const int G = Hq / Hkv;
   const int n_qt = (T + BM - 1) / BM;
-  const int BH = B * Hq;
-  int qt = blockIdx.x / BH;
-  const int bh = blockIdx.x - qt * BH;
-  if (causal) qt = n_qt - 1 - qt;  // heaviest query tiles first
-  const int b = bh / Hq;
-  const int h = bh - b * Hq;
-  const int kvh = h / (Hq / Hkv);
+  int gi, rank;
+  decode_unit(blockIdx.x, B * Hkv, gi, rank);
+  const int b = gi / Hkv;
+  const int kvh = gi - b * Hkv;
+  const int hh = rank % G;
+  const int qt = causal ? n_qt - 1 - rank / G : rank / G;  // heaviest tiles first
+  const int h = kvh * G + hh;
 
-  const size_t q_stride = (size_t)Hq * kHeadDim;   // elements between tokens of q / o
-  const size_t kv_stride = (size_t)Hkv * kHeadDim;  // elements between tokens of k / v
-  const uint16_t* qbase = q + ((size_t)b * T * Hq + h) * kHeadDim;
-  const uint16_t* kbase = k + ((size_t)b * T * Hkv + kvh) * kHeadDim;
-  const uint16_t* vbase = v + ((size_t)b * T * Hkv + kvh) * kHeadDim;
+  // Per-batch-element buffers; byte offsets below are within one batch element.
+  const uint32_t q_row = (uint32_t)Hq * kHeadDim * 2;   // bytes between tokens of q / o
+  const uint32_t kv_row = (uint32_t)Hkv * kHeadDim * 2;  // bytes between tokens of k / v
+  const size_t qe = (size_t)T * Hq * kHeadDim, ke = (size_t)T * Hkv * kHeadDim;
+  const rsrc_t rk = make_rsrc(k + b * ke, (uint32_t)T * kv_row);
+  const rsrc_t rv = make_rsrc(v + b * ke, (uint32_t)T * kv_row);
 
-  const int qw0 = qt * BM + wave * 32;  // first query row of this wave
-  const int my_q = qw0 + l32;           // the query row this lane accumulates
+  const int qw0 = qt * BM + 32 * qb;  // first query row of this wave
+  const int my_q = qw0 + l32;         // the query row this lane accumulates
+  const uint32_t qoff = (uint32_t)my_q * q_row + (uint32_t)h * kHeadDim * 2;  // bytes
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query my_q, d = 16s + 8g + [0, 8).
+  const rsrc_t rq = make_rsrc(q + b * qe, (uint32_t)T * q_row);
+  const rsrc_t ro = make_rsrc(o + b * qe, (uint32_t)T * q_row);
+  const rsrc_t rl = make_rsrc(lse + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
   u32x4_t qf[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    qf[s] = my_q < T ? gload16(qbase + (size_t)my_q * q_stride + 16 * s + 8 * g) : zero4u();
+  for (int s = 0; s < 4; ++s) qf[s] = bload16(rq, qoff + 32 * s + 16 * g);
+  wait_loads();
 
   f32x16_t oacc[2] = {zero16(), zero16()};  // O^T: rows d = 32*db + 8*(r/4) + 4g + r%4
   float m_run = -1e30f;                     // running max (base-2 units)
@@ -78,123 +93,128 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_bf16_kernel(
   const int kv_end = causal ? min(T, (qt + 1) * BM) : T;
   const int n_kv = (kv_end + BN - 1) / BN;
 
-  // Cooperative tile load: 64 rows x 8 chunks of 16 bytes per tensor, two chunks
-  // of each tensor per thread; a wave instruction covers 8 whole rows.
-  u32x4_t kreg[2], vreg[2];
-  auto gload_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + NTHREADS * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      const int key = kt * BN + row;
-      kreg[i] = key < T ? gload16(kbase + (size_t)key * kv_stride + col) : zero4u();
-      vreg[i] = key < T ? gload16(vbase + (size_t)key * kv_stride + col) : zero4u();
-    }
+  const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
+  const uint32_t ld_off = (uint32_t)ld_row * kv_row + (uint32_t)kvh * kHeadDim * 2 + 2 * ld_col;
+  u32x4_t kreg, vreg;
+  auto gload_tile = [&](int kt) {  // rows past the sequence end read as zero
+    const uint32_t off = ld_off + (uint32_t)(kt * BN) * kv_row;
+    kreg = bload16(rk, off);
+    vreg = bload16(rv, off);
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + NTHREADS * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      lds_store16(sK + row * PITCH + col, kreg[i]);
-      lds_store16(sV + row * PITCH + col, vreg[i]);
-    }
+  auto store_tile = [&](int buf) {
+    lds_store16(smem + (2 * buf) * TILE + ld_row * PITCH + ld_col, kreg);
+    lds_store16(smem + (2 * buf + 1) * TILE + ld_row * PITCH + ld_col, vreg);
   };
 
   gload_tile(0);
-  store_tile();
+  store_tile(0);
   __syncthreads();
 
   for (int kt = 0; kt < n_kv; ++kt) {
+    const int cur = kt & 1;
     if (kt + 1 < n_kv) gload_tile(kt + 1);  // next tile's loads overlap this tile's math
-    const int k0 = kt * BN;
-    const bool active = !causal || k0 <= qw0 + 31;
+    const uint16_t* sK = smem + (2 * cur) * TILE;
+    const uint16_t* sV = smem + (2 * cur + 1) * TILE;
+    const int kb0 = kt * BN + 32 * kh;
+    const bool active = kb0 < T && (!causal || kb0 <= qw0 + 31);
     if (active) {
-      // S^T (64 keys x 32 queries) as two 32x32 blocks.
-      f32x16_t sacc[2] = {zero16(), zero16()};
+      f32x16_t sacc = zero16();
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4_t a = lds_load16(sK + (32 * mb + l32) * PITCH + 16 * s + 8 * g);
-          sacc[mb] = mfma_32x32x16(a, qf[s], sacc[mb]);
-        }
-      }
-      const bool need_mask = (causal && k0 + BN - 1 > qw0) || (k0 + BN > T);
+      for (int s = 0; s < 4; ++s)
+        sacc = mfma_32x32x16(lds_load16(sK + (32 * kh + l32) * PITCH + 16 * s + 8 * g), qf[s], sacc);
+      // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.
       float mx = -__builtin_inff();
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      if ((causal && kb0 + 31 > qw0) || kb0 + 32 > T) {
+        // Diagonal tile or sequence tail: keys after the query or past the end
+        // get -inf.
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float sv = sacc[mb][r] * scale_log2;
-          if (need_mask) {
-            const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if ((causal && key > my_q) || key >= T) sv = -__builtin_inff();
-          }
-          sacc[mb][r] = sv;
+          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const float sv = ((causal && key > my_q) || key >= T) ? -__builtin_inff() : sacc[r] * scale_log2;
+          sacc[r] = sv;
           mx = fmaxf(mx, sv);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] *= scale_log2;
+          mx = fmaxf(mx, sacc[r]);
         }
       }
       mx = halves_max(mx);
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[mb][r] - m_new);
-          sacc[mb][r] = p;
-          rs += p;
-        }
-      }
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      // O^T += V^T P^T over the four 16-key steps of the tile.
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t pb = pack_operand(sacc[ks >> 1], 8 * (ks & 1));
+      if (__any(m_new != m_run)) {
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const u32x4_t a = lds_operand_T(sV, PITCH, 16 * ks, 32 * db, lane);
-          oacc[db] = mfma_32x32x16(a, pb, oacc[db]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
+        m_run = m_new;
+      }
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(sacc[r] - m_run);
+        sacc[r] = p;
+        rs += p;
+      }
+      l_run += rs;
+      const u32x4_t pb0 = pack_operand(sacc, 0), pb1 = pack_operand(sacc, 8);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        oacc[db] = mfma_32x32x16(lds_operand_T(sV, PITCH, 32 * kh, 32 * db, lane), pb0, oacc[db]);
+        oacc[db] = mfma_32x32x16(lds_operand_T(sV, PITCH, 32 * kh + 16, 32 * db, lane), pb1, oacc[db]);
       }
     }
+    if (kt + 1 < n_kv) store_tile(cur ^ 1);
     __syncthreads();
-    if (kt + 1 < n_kv) {
-      store_tile();
-      __syncthreads();
-    }
   }
 
-  const float l_tot = halves_sum(l_run);
-  if (my_q < T) {
+  // Merge the key halves: (m, l, O) of half 1 into half 0, in that order.
+  float* part = reinterpret_cast<float*>(smem);
+  float* slot = part + (qb * 64 + lane) * PART_STRIDE;
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 4)
+        *reinterpret_cast<float4*>(slot + 16 * db + r) =
+            make_float4(oacc[db][r], oacc[db][r + 1], oacc[db][r + 2], oacc[db][r + 3]);
+    }
+    slot[32] = m_run;
+    slot[33] = l_run;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = slot[32], l1 = slot[33];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = fast_exp2(m_run - m), a1 = fast_exp2(m1 - m);
+    const float l_tot = halves_sum(l_run * a0 + l1 * a1);
+    // Rows past the sequence end are dropped by the buffer range check.
     const float inv = 1.0f / l_tot;
-    uint16_t* orow = o + ((size_t)b * T + my_q) * q_stride + (size_t)h * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const float4 x = *reinterpret_cast<const float4*>(slot + 16 * db + 4 * j);
         u32x2_t w;
-        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + 32 * db + 8 * j + 4 * g) = w;
+        w[0] = pack_bf16x2((oacc[db][4 * j + 0] * a0 + x.x * a1) * inv,
+                           (oacc[db][4 * j + 1] * a0 + x.y * a1) * inv);
+        w[1] = pack_bf16x2((oacc[db][4 * j + 2] * a0 + x.z * a1) * inv,
+                           (oacc[db][4 * j + 3] * a0 + x.w * a1) * inv);
+        bstore8(ro, qoff + 2 * (32 * db + 8 * j + 4 * g), w);
       }
     }
-    if (g == 0) lse[((size_t)b * Hq + h) * T + my_q] = (m_run + fast_log2(l_tot)) * kLn2;
+    if (g == 0 && my_q < T) bstore_f32(rl, ((uint32_t)h * T + my_q) * 4, (m + fast_log2(l_tot)) * kLn2);
   }
 }
 
 }  // namespace
 
 const char* fwd_bf16_tiles() {
-  return "fwd_bf16{BM=128,BN=64,waves=4,mfma=32x32x16}";
+  return "fwd_bf16{BM=128,BN=64,waves=8(4 query x 2 key),mfma=32x32x16}";
 }
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,

@@ -40,7 +40,8 @@ hipError_t launch_bwd_dq_f32(const Problem& p, const void* q, const void* k, con
 
 // Tile constants of each kernel family, reported by attn_build_info().
 const char* fwd_bf16_tiles();
-const char* bwd_bf16_tiles();
+const char* bwd_dkdv_tiles();
+const char* bwd_dq_tiles();
 const char* f32_tiles();
 
 }  // namespace rca

@@ -87,6 +87,7 @@ FWD_ERRORS = [
     ("scale_inf", dict(scale=float("inf")), A.ATTN_ERR_INVALID_ARG),
     ("T_too_long", dict(T=(1 << 24) + 1), A.ATTN_ERR_INVALID_ARG),
     ("too_many_tiles", dict(B=1 << 14, T=1 << 16, Hq=8, Hkv=8), A.ATTN_ERR_INVALID_ARG),
+    ("batch_element_too_large", dict(B=1, T=1 << 20, Hq=128, Hkv=128), A.ATTN_ERR_INVALID_ARG),
     ("head_dim_128", dict(D=128), A.ATTN_ERR_UNSUPPORTED),
     ("unknown_dtype", dict(dtype=7), A.ATTN_ERR_UNSUPPORTED),
     ("o_overlaps_q", dict(o=BASE + 64), A.ATTN_ERR_INVALID_ARG),
