@@ -70,6 +70,12 @@ __device__ __forceinline__ u32x4_t pack_operand(const f32x16_t& acc, int r0) {
   return o;
 }
 
+// acc + lo(w) + hi(w) for the two bf16 halves of w (v_dot2c_f32_bf16 against ones).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -20,7 +20,10 @@
 //     half-wave exchange (v_permlane32_swap), and O^T += V^T P^T takes the
 //     probabilities straight from the accumulators (packed to bf16, round to
 //     nearest even) with V^T read from the row-major tile by ds_read_b64_tr_b16;
-//   * the output rescale is skipped when no row's running max moved;
+//   * the running max moves lazily (only when a row's maximum grew by more than
+//     2^8), so the output rescale runs a few times per row instead of per tile;
+//     the row sums are accumulated from the packed bf16 probabilities with
+//     v_dot2c_f32_bf16;
 //   * scores are kept in base-2 units (scale * log2 e folded in) so every
 //     exponential is one v_exp_f32;
 //   * the two key halves' states (max, sum, O) are merged in a fixed order;
@@ -40,8 +43,10 @@ constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
 constexpr int TILE = BN * PITCH;
 constexpr int PART_STRIDE = 36;  // floats per lane in the merge buffer (32 of O, m, l)
+constexpr float kSlack = 8.0f;   // lazy-rescale threshold, base-2 units
 static_assert(4 * 64 * PART_STRIDE * 4 <= 4 * TILE * 2, "merge buffer must fit");
 
+template <bool kPosScale>
 __global__ __launch_bounds__(NTHREADS) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv,
@@ -122,46 +127,57 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         sacc = mfma_32x32x16(lds_load16(sK + (32 * kh + l32) * PITCH + 16 * s + 8 * g), qf[s], sacc);
-      // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.
-      float mx = -__builtin_inff();
-      if ((causal && kb0 + 31 > qw0) || kb0 + 32 > T) {
+      // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.  The
+      // tile maximum is taken over the raw scores (the scale is positive; for a
+      // negative scale the minimum) and scaled once.
+      const bool edge = (causal && kb0 + 31 > qw0) || kb0 + 32 > T;
+      bool keep[16];
+      float mraw;
+      if (edge) {
         // Diagonal tile or sequence tail: keys after the query or past the end
-        // get -inf.
+        // take no part in the maximum and get probability 0.
+        mraw = kPosScale ? -__builtin_inff() : __builtin_inff();
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const float sv = ((causal && key > my_q) || key >= T) ? -__builtin_inff() : sacc[r] * scale_log2;
-          sacc[r] = sv;
-          mx = fmaxf(mx, sv);
+          keep[r] = !((causal && key > my_q) || key >= T);
+          const float x = keep[r] ? sacc[r] : (kPosScale ? -__builtin_inff() : __builtin_inff());
+          mraw = kPosScale ? fmaxf(mraw, x) : fminf(mraw, x);
         }
       } else {
+        mraw = sacc[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[r] *= scale_log2;
-          mx = fmaxf(mx, sacc[r]);
-        }
+        for (int r = 1; r < 16; ++r) mraw = kPosScale ? fmaxf(mraw, sacc[r]) : fminf(mraw, sacc[r]);
       }
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new != m_run)) {
-        const float alpha = fast_exp2(m_run - m_new);
+      const float mx = halves_max(mraw * scale_log2);
+      // Lazy rescale: the running max only moves when some row's maximum grew by
+      // more than kSlack (base-2 units), so probabilities stay below 2^kSlack
+      // (exact in bf16 and fp32) and O is rescaled a few times per row, not per tile.
+      const float m_cand = fmaxf(m_run, mx);
+      if (__any(m_cand > m_run + kSlack)) {
+        const float alpha = fast_exp2(m_run - m_cand);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
-        m_run = m_new;
+        m_run = m_cand;
       }
-      float rs = 0.f;
+      if (edge) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(sacc[r] - m_run);
-        sacc[r] = p;
-        rs += p;
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[r], scale_log2, -m_run));
+          sacc[r] = keep[r] ? p : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], scale_log2, -m_run));
       }
-      l_run += rs;
       const u32x4_t pb0 = pack_operand(sacc, 0), pb1 = pack_operand(sacc, 8);
+      // Row sum of the bf16 probabilities that enter O (two per v_dot2c_f32_bf16).
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run = add_bf16_pair(pb1[i], add_bf16_pair(pb0[i], l_run));
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         oacc[db] = mfma_32x32x16(lds_operand_T(sV, PITCH, 32 * kh, 32 * db, lane), pb0, oacc[db]);
@@ -221,7 +237,8 @@ hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const
                            float* lse, hipStream_t s) {
   const int n_qt = (p.T + BM - 1) / BM;
   const dim3 grid((unsigned)(n_qt * p.B * p.Hq));
-  attn_fwd_bf16_kernel<<<grid, NTHREADS, 0, s>>>(
+  auto kernel = p.scale_log2 >= 0.f ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>;
+  kernel<<<grid, NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, p.B, p.T, p.Hq, p.Hkv,
       p.scale_log2, p.causal);
