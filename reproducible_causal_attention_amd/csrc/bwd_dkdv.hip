@@ -19,12 +19,13 @@
 //   * the work of one key block is a fixed list of steps (query head of the
 //     group, 32-query block); wave w takes steps w, w+8, w+16, ... and keeps its
 //     own fp32 partial dK^T, dV^T in accumulator registers;
-//   * per step the wave loads the 32 query rows of q and dO straight from HBM in
-//     the MFMA A-operand layout (issued a step ahead), computes S = Q K^T and
+//   * per step the wave copies the 32 query rows of q and dO (loaded from HBM
+//     during its previous step) to a wave-private LDS region, immediately
+//     issues the loads of its next step, computes S = Q K^T and
 //     dP = dO V^T with the keys on the lanes, then P and dS, packs them from the
 //     accumulators into B operands and adds dO^T P and Q^T dS into dV^T and dK^T;
-//     the transposed A operands come from a copy of the rows in a wave-private
-//     LDS region read with ds_read_b64_tr_b16;
+//     the transposed A operands are read from the same LDS rows with
+//     ds_read_b64_tr_b16;
 //   * all loads and stores are buffer instructions whose range check supplies
 //     the zero rows past the sequence end, and step indexing is scalar;
 //   * the eight partials are summed through LDS in wave order 0..7 and written
@@ -129,30 +130,27 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
       R.stat = g == 0 ? bload_f32(rl, soff) * kLog2e : bload_f32(rd, soff);
     };
 
-    StepRegs R;
-    if (wave < nsteps) load_step(wave, R);
-    for (int s = wave; s < nsteps; s += NWAVES) {
+    // One step: copy its rows to the wave's LDS region, refill the registers with
+    // the rows of this wave's next step (in flight for the whole step), then
+    // compute from LDS.
+    auto step = [&](int s, StepRegs& R) {
       const int hh = s / per_head;
       const int qb = qb0 + (s - hh * per_head);
       const int q0 = 32 * qb;
-      // Row-major copy of this step's rows for the transposed reads, and the row
-      // statistics, to be read back in the accumulator layout.
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         lds_store16(myQ + l32 * PITCH + 16 * c + 8 * g, R.qa[c]);
         lds_store16(mydO + l32 * PITCH + 16 * c + 8 * g, R.da[c]);
       }
       mystat[lane] = R.stat;
-      f32x16_t sacc = mfma_32x32x16(R.qa[0], kf[0], zero16());
-      f32x16_t pacc = mfma_32x32x16(R.da[0], vf[0], zero16());
-#pragma unroll
-      for (int c = 1; c < 4; ++c) {
-        sacc = mfma_32x32x16(R.qa[c], kf[c], sacc);
-        pacc = mfma_32x32x16(R.da[c], vf[c], pacc);
-      }
-      // The next step's loads reuse R's registers and fly while this step finishes.
       if (s + NWAVES < nsteps) load_step(s + NWAVES, R);
       wave_lds_fence();
+      f32x16_t sacc = zero16(), pacc = zero16();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sacc = mfma_32x32x16(lds_load16(myQ + l32 * PITCH + 16 * c + 8 * g), kf[c], sacc);
+        pacc = mfma_32x32x16(lds_load16(mydO + l32 * PITCH + 16 * c + 8 * g), vf[c], pacc);
+      }
       // Register r holds query q0 + 8*(r/4) + 4g + r%4 against key my_key.
       float Lr[16], Dr[16];
 #pragma unroll
@@ -191,7 +189,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
         dk_acc[db] = mfma_32x32x16(lds_operand_T(myQ, PITCH, 16, 32 * db, lane), sb1, dk_acc[db]);
       }
       wave_lds_fence();  // this step's LDS reads complete before the next step's writes
-    }
+    };
+
+    StepRegs R;
+    if (wave < nsteps) load_step(wave, R);
+    for (int s = wave; s < nsteps; s += NWAVES) step(s, R);
 
     // Sum the eight partials in wave order and write dK (scaled) and dV once.
     float* part = reinterpret_cast<float*>(smem);
