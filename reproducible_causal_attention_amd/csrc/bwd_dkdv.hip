@@ -20,7 +20,8 @@
 //     group, 32-query block); wave w takes steps w, w+8, w+16, ... and keeps its
 //     own fp32 partial dK^T, dV^T in accumulator registers;
 //   * per step the wave copies the 32 query rows of q and dO (loaded from HBM
-//     during its previous step) to a wave-private LDS region, immediately
+//     during its previous step, eight whole rows per load instruction) to a
+//     wave-private LDS region, immediately
 //     issues the loads of its next step, computes S = Q K^T and
 //     dP = dO V^T with the keys on the lanes, then P and dS, packs them from the
 //     accumulators into B operands and adds dO^T P and Q^T dS into dV^T and dK^T;
@@ -44,12 +45,14 @@ constexpr int PART_STRIDE = 36;               // floats per lane in the partial-
 constexpr int SMEM_BYTES = NWAVES * REGION * 2;
 static_assert(NWAVES * 64 * PART_STRIDE * 4 <= SMEM_BYTES, "reduction buffer must fit");
 
-// One step's operands: 32 query rows of q and dO in the A-operand layout, and
-// one row statistic per lane (lanes 0..31: lse of row l in base-2 units,
-// lanes 32..63: delta of row l-32).
+// One step's operands as loaded: register i of qa (da) holds 16 bytes of q (dO)
+// row 8i + lane/8 of the step's 32 query rows, bytes 16*(lane%8) .. +15, so each
+// load instruction reads eight whole 128-byte rows; lse and delta belong to
+// query row lane % 32.  Nothing reads them until the next step copies them to
+// LDS, so the loads stay in flight for a whole step.
 struct StepRegs {
   u32x4_t qa[4], da[4];
-  float stat;
+  float lse, delta;
 };
 
 __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
@@ -90,6 +93,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
   float* mystat = reinterpret_cast<float*>(mydO + 32 * PITCH);  // [0,32): lse*log2e, [32,64): delta
   // This lane's 16-byte chunk of a row in the A-operand layout (chunk c adds 32 bytes).
   const uint32_t lane_col = 16u * g;
+  // Row staging: lane copies chunk lane % 8 of rows 8i + lane / 8.
+  const int st_row = lane >> 3, st_col = 8 * (lane & 7);
 
   for (int half = 0; half < 2; ++half) {
     const int j = half == 0 ? pair : nkb - 1 - pair;
@@ -119,15 +124,16 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
       const int hh = s / per_head;  // scalar
       const int qb = qb0 + (s - hh * per_head);
       const int h = kvh * G + hh;
-      const int row = 32 * qb + l32;
-      const uint32_t off = (uint32_t)row * q_row + (uint32_t)h * kHeadDim * 2 + lane_col;
+      const uint32_t off =
+          (uint32_t)(32 * qb + st_row) * q_row + (uint32_t)h * kHeadDim * 2 + 2 * st_col;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        R.qa[c] = bload16(rq, off + 32 * c);
-        R.da[c] = bload16(rdo, off + 32 * c);
+      for (int i = 0; i < 4; ++i) {
+        R.qa[i] = bload16s(rq, off, (uint32_t)(8 * i) * q_row);
+        R.da[i] = bload16s(rdo, off, (uint32_t)(8 * i) * q_row);
       }
-      const uint32_t soff = ((uint32_t)h * T + row) * 4;
-      R.stat = g == 0 ? bload_f32(rl, soff) * kLog2e : bload_f32(rd, soff);
+      const uint32_t soff = ((uint32_t)h * T + 32 * qb + l32) * 4;
+      R.lse = bload_f32(rl, soff);
+      R.delta = bload_f32(rd, soff);
     };
 
     // One step: copy its rows to the wave's LDS region, refill the registers with
@@ -138,11 +144,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
       const int qb = qb0 + (s - hh * per_head);
       const int q0 = 32 * qb;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        lds_store16(myQ + l32 * PITCH + 16 * c + 8 * g, R.qa[c]);
-        lds_store16(mydO + l32 * PITCH + 16 * c + 8 * g, R.da[c]);
+      for (int i = 0; i < 4; ++i) {
+        lds_store16(myQ + (8 * i + st_row) * PITCH + st_col, R.qa[i]);
+        lds_store16(mydO + (8 * i + st_row) * PITCH + st_col, R.da[i]);
       }
-      mystat[lane] = R.stat;
+      mystat[lane] = g == 0 ? R.lse * kLog2e : R.delta;  // lanes 0..31: lse in base 2
       if (s + NWAVES < nsteps) load_step(s + NWAVES, R);
       wave_lds_fence();
       f32x16_t sacc = zero16(), pacc = zero16();
