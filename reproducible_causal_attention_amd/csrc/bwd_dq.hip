@@ -82,15 +82,13 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
     qf[s] = bload16(rq, qoff + 32 * s + 16 * g);
     df[s] = bload16(rdo, qoff + 32 * s + 16 * g);
   }
+  // Rows past the sequence end read lse = delta = 0 (buffer range check) and are
+  // never stored.
   const rsrc_t rl = make_rsrc(lse + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
   const rsrc_t rdl = make_rsrc(delta + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
-  // Rows past the sequence end are never stored; give them neutral statistics.
-  const float L2 = my_q < T ? bload_f32(rl, ((uint32_t)h * T + my_q) * 4) * kLog2e : 0.f;
-  const float Dl = my_q < T ? bload_f32(rdl, ((uint32_t)h * T + my_q) * 4) : 0.f;
-  wait_loads();
-  f32x16_t neg_delta;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) neg_delta[r] = -Dl;
+  const uint32_t stat_off = ((uint32_t)h * T + my_q) * 4;
+  const float lse_raw = bload_f32(rl, my_q < T ? stat_off : 0xffffffffu);
+  const float Dl = bload_f32(rdl, my_q < T ? stat_off : 0xffffffffu);
 
   f32x16_t dq_acc[2] = {zero16(), zero16()};  // dQ^T: rows d = 32*db + 8*(r/4) + 4g + r%4
 
@@ -112,7 +110,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
     lds_store16(smem + (2 * buf + 1) * TILE + ld_row * PITCH + ld_col, vreg);
   };
 
-  gload_tile(0);
+  gload_tile(0);  // in flight together with the row loads above
+  wait_loads();
+  const float L2 = lse_raw * kLog2e;
+  f32x16_t neg_delta;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_delta[r] = -Dl;
   store_tile(0);
   __syncthreads();
 
