@@ -19,16 +19,17 @@
 //   * the work of one key block is a fixed list of steps (query head of the
 //     group, 32-query block); wave w takes steps w, w+8, w+16, ... and keeps its
 //     own fp32 partial dK^T, dV^T in accumulator registers;
-//   * per step the wave copies the 32 query rows of q and dO (loaded from HBM
-//     during its previous step, eight whole rows per load instruction) to a
-//     wave-private LDS region, immediately
-//     issues the loads of its next step, computes S = Q K^T and
-//     dP = dO V^T with the keys on the lanes, then P and dS, packs them from the
-//     accumulators into B operands and adds dO^T P and Q^T dS into dV^T and dK^T;
-//     the transposed A operands are read from the same LDS rows with
-//     ds_read_b64_tr_b16;
-//   * all loads and stores are buffer instructions whose range check supplies
-//     the zero rows past the sequence end, and step indexing is scalar;
+//   * the 32 query rows of q and dO of a step go straight from HBM into a
+//     wave-private, double-buffered LDS region (buffer_load ... lds, eight whole
+//     rows per instruction, XOR-swizzled 16-byte chunks), issued one step
+//     ahead; lse and delta of the rows travel through registers and are stored
+//     next to them, delta negated, so the dP accumulator starts at -delta and
+//     the products leave dP - delta directly;
+//   * S = Q K^T and dP = dO V^T put the keys on the lanes; P and dS are packed
+//     from the accumulators into B operands, and dO^T P and Q^T dS are added into
+//     dV^T and dK^T with the transposed A operands read by ds_read_b64_tr_b16;
+//   * K and V of the key block are staged once through LDS and held in
+//     registers as the B operands of S and dP;
 //   * the eight partials are summed through LDS in wave order 0..7 and written
 //     once (dK scaled by the softmax scale), in bf16 with round to nearest even.
 #include "cdna4.hpp"
@@ -37,30 +38,23 @@
 namespace rca {
 namespace {
 
-constexpr int PITCH = 72;                     // LDS row pitch (bf16 elements)
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int REGION = 2 * 32 * PITCH + 128;  // one wave's Q rows, dO rows, 64 row stats (bf16 units)
-constexpr int PART_STRIDE = 36;               // floats per lane in the partial-sum buffer
-constexpr int SMEM_BYTES = NWAVES * REGION * 2;
-static_assert(NWAVES * 64 * PART_STRIDE * 4 <= SMEM_BYTES, "reduction buffer must fit");
-
-// One step's operands as loaded: register i of qa (da) holds 16 bytes of q (dO)
-// row 8i + lane/8 of the step's 32 query rows, bytes 16*(lane%8) .. +15, so each
-// load instruction reads eight whole 128-byte rows; lse and delta belong to
-// query row lane % 32.  Nothing reads them until the next step copies them to
-// LDS, so the loads stay in flight for a whole step.
-struct StepRegs {
-  u32x4_t qa[4], da[4];
-  float lse, delta;
-};
+constexpr int ROWS_BYTES = 32 * 128;                   // 32 swizzled rows of 64 bf16
+constexpr int BUF_BYTES = 2 * ROWS_BYTES + 256;        // q rows, dO rows, 64 row statistics
+constexpr int WAVE_BYTES = 2 * BUF_BYTES;              // double-buffered
+constexpr int KV_OFF = NWAVES * WAVE_BYTES;            // staging of the block's K and V rows
+constexpr int SMEM_BYTES = KV_OFF + 2 * ROWS_BYTES;
+constexpr int PART_BYTES = NWAVES * 16 * 64 * 16;      // [wave][16 float4 per lane][lane]
+static_assert(PART_BYTES <= SMEM_BYTES, "reduction buffer must fit");
+static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
 
 __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
     float scale, float scale_log2, int causal) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NWAVES * REGION];
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -79,22 +73,22 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
   const uint32_t q_row = (uint32_t)Hq * kHeadDim * 2;   // bytes between tokens of q / dO
   const uint32_t kv_row = (uint32_t)Hkv * kHeadDim * 2;  // bytes between tokens of k / v
   const size_t qe = (size_t)T * Hq * kHeadDim, ke = (size_t)T * Hkv * kHeadDim;
-  const rsrc_t rq = make_rsrc(q + b * qe, (uint32_t)T * q_row);
-  const rsrc_t rdo = make_rsrc(dO + b * qe, (uint32_t)T * q_row);
-  const rsrc_t rk = make_rsrc(k + b * ke, (uint32_t)T * kv_row);
-  const rsrc_t rv = make_rsrc(v + b * ke, (uint32_t)T * kv_row);
   const rsrc_t rdk = make_rsrc(dk + b * ke, (uint32_t)T * kv_row);
   const rsrc_t rdv = make_rsrc(dv + b * ke, (uint32_t)T * kv_row);
+  const u32x4_t q_src = raw_rsrc(q + b * qe, (uint32_t)T * q_row);   // load-to-LDS sources
+  const u32x4_t do_src = raw_rsrc(dO + b * qe, (uint32_t)T * q_row);
+  const u32x4_t k_src = raw_rsrc(k + b * ke, (uint32_t)T * kv_row);
+  const u32x4_t v_src = raw_rsrc(v + b * ke, (uint32_t)T * kv_row);
   const rsrc_t rl = make_rsrc(lse + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
   const rsrc_t rd = make_rsrc(delta + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
 
-  uint16_t* myQ = smem + wave * REGION;
-  uint16_t* mydO = myQ + 32 * PITCH;
-  float* mystat = reinterpret_cast<float*>(mydO + 32 * PITCH);  // [0,32): lse*log2e, [32,64): delta
-  // This lane's 16-byte chunk of a row in the A-operand layout (chunk c adds 32 bytes).
-  const uint32_t lane_col = 16u * g;
-  // Row staging: lane copies chunk lane % 8 of rows 8i + lane / 8.
-  const int st_row = lane >> 3, st_col = 8 * (lane & 7);
+  char* const my_region = smem + wave * WAVE_BYTES;
+  const uint16_t* const sK = reinterpret_cast<const uint16_t*>(smem + KV_OFF);
+  const uint16_t* const sV = reinterpret_cast<const uint16_t*>(smem + KV_OFF + ROWS_BYTES);
+  // Load-to-LDS lane mapping: lane fills slot lane % 8 of row 8i + lane / 8 of an
+  // instruction's eight rows, i.e. it fetches chunk swz_slot(row, lane % 8).
+  const int dma_row = lane >> 3;
+  auto dma_chunk_bytes = [&](int row) { return 16u * (uint32_t)swz_slot(row, lane & 7); };
 
   for (int half = 0; half < 2; ++half) {
     const int j = half == 0 ? pair : nkb - 1 - pair;
@@ -102,71 +96,85 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
     const int k0 = 32 * j;
     const int my_key = k0 + l32;
 
-    // K^T and V^T as B operands (keys on the lanes): d = 16s + 8g + [0, 8).
-    u32x4_t kf[4], vf[4];
-    {
-      const uint32_t off = (uint32_t)my_key * kv_row + (uint32_t)kvh * kHeadDim * 2 + lane_col;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        kf[s] = bload16(rk, off + 32 * s);
-        vf[s] = bload16(rv, off + 32 * s);
-      }
-      wait_loads();
-    }
-    f32x16_t dk_acc[2] = {zero16(), zero16()};  // dK^T: rows d = 32*db + 8*(r/4) + 4g + r%4
-    f32x16_t dv_acc[2] = {zero16(), zero16()};
-
     const int qb0 = causal ? j : 0;  // first query block that sees key block j
     const int per_head = nkb - qb0;
     const int nsteps = G * per_head;
 
-    auto load_step = [&](int s, StepRegs& R) {
+    // Step s: rows 32*qb .. +31 of query head h of the group.  Issues the copy
+    // of its q and dO rows into buffer buf of this wave's region, and returns
+    // the loads of the rows' lse and delta.
+    auto issue_step = [&](int s, int buf, float& l_raw, float& d_raw) {
       const int hh = s / per_head;  // scalar
       const int qb = qb0 + (s - hh * per_head);
       const int h = kvh * G + hh;
-      const uint32_t off =
-          (uint32_t)(32 * qb + st_row) * q_row + (uint32_t)h * kHeadDim * 2 + 2 * st_col;
+      char* dst = my_region + buf * BUF_BYTES;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        R.qa[i] = bload16s(rq, off, (uint32_t)(8 * i) * q_row);
-        R.da[i] = bload16s(rdo, off, (uint32_t)(8 * i) * q_row);
+        const int r = 8 * i + dma_row;
+        const uint32_t off = (uint32_t)(32 * qb + r) * q_row + (uint32_t)h * kHeadDim * 2 + dma_chunk_bytes(r);
+        dma16(q_src, dst + 1024 * i, off);
+        dma16(do_src, dst + ROWS_BYTES + 1024 * i, off);
       }
       const uint32_t soff = ((uint32_t)h * T + 32 * qb + l32) * 4;
-      R.lse = bload_f32(rl, soff);
-      R.delta = bload_f32(rd, soff);
+      l_raw = bload_f32(rl, soff);
+      d_raw = bload_f32(rd, soff);
     };
 
-    // One step: copy its rows to the wave's LDS region, refill the registers with
-    // the rows of this wave's next step (in flight for the whole step), then
-    // compute from LDS.
-    auto step = [&](int s, StepRegs& R) {
+    // Prologue: K and V rows of the block (wave w copies eight rows of K for
+    // w < 4, of V for w >= 4) and this wave's first step.
+    float l_raw = 0.f, d_raw = 0.f;
+    {
+      const int r = 8 * (wave & 3) + dma_row;
+      const uint32_t off = (uint32_t)(k0 + r) * kv_row + (uint32_t)kvh * kHeadDim * 2 + dma_chunk_bytes(r);
+      char* dst = smem + KV_OFF + (wave >> 2) * ROWS_BYTES + 1024 * (wave & 3);
+      dma16(wave < 4 ? k_src : v_src, dst, off);
+    }
+    if (wave < nsteps) issue_step(wave, 0, l_raw, d_raw);
+    wait_loads();
+    __syncthreads();
+
+    // K^T and V^T as B operands (keys on the lanes): d = 16c + 8g + [0, 8).
+    u32x4_t kf[4], vf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      kf[c] = lds_load16_swz(sK, l32, 16 * c + 8 * g);
+      vf[c] = lds_load16_swz(sV, l32, 16 * c + 8 * g);
+    }
+    f32x16_t dk_acc[2] = {zero16(), zero16()};  // dK^T: rows d = 32*db + 8*(r/4) + 4g + r%4
+    f32x16_t dv_acc[2] = {zero16(), zero16()};
+
+    int buf = 0;
+    for (int s = wave; s < nsteps; s += NWAVES, buf ^= 1) {
       const int hh = s / per_head;
-      const int qb = qb0 + (s - hh * per_head);
-      const int q0 = 32 * qb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lds_store16(myQ + (8 * i + st_row) * PITCH + st_col, R.qa[i]);
-        lds_store16(mydO + (8 * i + st_row) * PITCH + st_col, R.da[i]);
-      }
-      mystat[lane] = g == 0 ? R.lse * kLog2e : R.delta;  // lanes 0..31: lse in base 2
-      if (s + NWAVES < nsteps) load_step(s + NWAVES, R);
+      const int q0 = 32 * (qb0 + (s - hh * per_head));
+      char* cur = my_region + buf * BUF_BYTES;
+      const uint16_t* sQ = reinterpret_cast<const uint16_t*>(cur);
+      const uint16_t* sdO = reinterpret_cast<const uint16_t*>(cur + ROWS_BYTES);
+      float* stat = reinterpret_cast<float*>(cur + 2 * ROWS_BYTES);  // [0,32): lse*log2e, [32,64): -delta
+
+      wait_loads();  // this step's rows and statistics (issued one step ago)
+      stat[lane] = g == 0 ? l_raw * kLog2e : -d_raw;
+      if (s + NWAVES < nsteps) issue_step(s + NWAVES, buf ^ 1, l_raw, d_raw);
       wave_lds_fence();
-      f32x16_t sacc = zero16(), pacc = zero16();
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        sacc = mfma_32x32x16(lds_load16(myQ + l32 * PITCH + 16 * c + 8 * g), kf[c], sacc);
-        pacc = mfma_32x32x16(lds_load16(mydO + l32 * PITCH + 16 * c + 8 * g), vf[c], pacc);
-      }
-      // Register r holds query q0 + 8*(r/4) + 4g + r%4 against key my_key.
-      float Lr[16], Dr[16];
+
+      // Register r of a 32x32 accumulator is query q0 + 8*(r/4) + 4g + r%4
+      // against key my_key, so float4 jj of the statistics fills registers 4jj..4jj+3.
+      f32x16_t pacc, Lr;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float4 l4 = *reinterpret_cast<const float4*>(mystat + 8 * jj + 4 * g);
-        const float4 d4 = *reinterpret_cast<const float4*>(mystat + 32 + 8 * jj + 4 * g);
+        const float4 d4 = *reinterpret_cast<const float4*>(stat + 32 + 8 * jj + 4 * g);
+        const float4 l4 = *reinterpret_cast<const float4*>(stat + 8 * jj + 4 * g);
+        pacc[4 * jj + 0] = d4.x; pacc[4 * jj + 1] = d4.y; pacc[4 * jj + 2] = d4.z; pacc[4 * jj + 3] = d4.w;
         Lr[4 * jj + 0] = l4.x; Lr[4 * jj + 1] = l4.y; Lr[4 * jj + 2] = l4.z; Lr[4 * jj + 3] = l4.w;
-        Dr[4 * jj + 0] = d4.x; Dr[4 * jj + 1] = d4.y; Dr[4 * jj + 2] = d4.z; Dr[4 * jj + 3] = d4.w;
       }
-      if ((causal && qb == j) || q0 + 31 >= T) {
+      f32x16_t sacc = zero16();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sacc = mfma_32x32x16(lds_load16_swz(sQ, l32, 16 * c + 8 * g), kf[c], sacc);
+        pacc = mfma_32x32x16(lds_load16_swz(sdO, l32, 16 * c + 8 * g), vf[c], pacc);
+      }
+      // pacc now holds dP - delta.
+      if ((causal && q0 == k0) || q0 + 31 >= T) {
         // Diagonal block or sequence tail: zero P where the key is after the
         // query or the query row does not exist.
 #pragma unroll
@@ -175,67 +183,66 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
           float p = fast_exp2(fmaf(sacc[r], scale_log2, -Lr[r]));
           p = ((causal && my_key > qi) || qi >= T) ? 0.f : p;
           sacc[r] = p;
-          pacc[r] = p * (pacc[r] - Dr[r]);
+          pacc[r] *= p;
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(sacc[r], scale_log2, -Lr[r]));
           sacc[r] = p;
-          pacc[r] = p * (pacc[r] - Dr[r]);
+          pacc[r] *= p;
         }
       }
       const u32x4_t pb0 = pack_operand(sacc, 0), pb1 = pack_operand(sacc, 8);
       const u32x4_t sb0 = pack_operand(pacc, 0), sb1 = pack_operand(pacc, 8);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        dv_acc[db] = mfma_32x32x16(lds_operand_T(mydO, PITCH, 0, 32 * db, lane), pb0, dv_acc[db]);
-        dk_acc[db] = mfma_32x32x16(lds_operand_T(myQ, PITCH, 0, 32 * db, lane), sb0, dk_acc[db]);
-        dv_acc[db] = mfma_32x32x16(lds_operand_T(mydO, PITCH, 16, 32 * db, lane), pb1, dv_acc[db]);
-        dk_acc[db] = mfma_32x32x16(lds_operand_T(myQ, PITCH, 16, 32 * db, lane), sb1, dk_acc[db]);
+        dv_acc[db] = mfma_32x32x16(lds_operand_T_swz(sdO, 0, 32 * db, lane), pb0, dv_acc[db]);
+        dk_acc[db] = mfma_32x32x16(lds_operand_T_swz(sQ, 0, 32 * db, lane), sb0, dk_acc[db]);
+        dv_acc[db] = mfma_32x32x16(lds_operand_T_swz(sdO, 16, 32 * db, lane), pb1, dv_acc[db]);
+        dk_acc[db] = mfma_32x32x16(lds_operand_T_swz(sQ, 16, 32 * db, lane), sb1, dk_acc[db]);
       }
-      wave_lds_fence();  // this step's LDS reads complete before the next step's writes
-    };
-
-    StepRegs R;
-    if (wave < nsteps) load_step(wave, R);
-    for (int s = wave; s < nsteps; s += NWAVES) step(s, R);
+      wave_lds_fence();  // this buffer's reads complete before it is refilled
+    }
 
     // Sum the eight partials in wave order and write dK (scaled) and dV once.
-    float* part = reinterpret_cast<float*>(smem);
-    const int kk = tid >> 4;  // key within the block, 0..31
-    const int c4 = tid & 15;  // 4-wide column chunk: d = 4*c4
-    const int src_lane = kk + 32 * (c4 & 1);
-    const int r0 = 16 * (c4 >> 3) + 4 * ((c4 & 7) >> 1);
-    const uint32_t out_off = (uint32_t)(k0 + kk) * kv_row + (uint32_t)kvh * kHeadDim * 2 + 8 * c4;
-    auto reduce_store = [&](const f32x16_t (&acc)[2], rsrc_t out, float f) {
-      __syncthreads();  // LDS free: every wave is past its previous use
-      float* mine = part + (wave * 64 + lane) * PART_STRIDE;
+    // Partial layout: [wave][float4 index f][lane], f = 0..7 dK, 8..15 dV, float4
+    // f of a tensor being accumulator registers 4f .. 4f+3 of the flat 32.
+    __syncthreads();  // every wave is past its last step: the regions are free
+    float4* part = reinterpret_cast<float4*>(smem);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 4)
-          *reinterpret_cast<float4*>(mine + 16 * db + r) =
-              make_float4(acc[db][r], acc[db][r + 1], acc[db][r + 2], acc[db][r + 3]);
-      }
-      __syncthreads();
-      float4 sum = *reinterpret_cast<const float4*>(part + src_lane * PART_STRIDE + r0);
+    for (int f = 0; f < 8; ++f) {
+      const f32x16_t& a = dk_acc[f >> 2];
+      const f32x16_t& c = dv_acc[f >> 2];
+      const int r = 4 * (f & 3);
+      part[(wave * 16 + f) * 64 + lane] = make_float4(a[r], a[r + 1], a[r + 2], a[r + 3]);
+      part[(wave * 16 + 8 + f) * 64 + lane] = make_float4(c[r], c[r + 1], c[r + 2], c[r + 3]);
+    }
+    __syncthreads();
+    {
+      // Thread -> (key kk, d = 4*c4 .. 4*c4+3): registers 16*db + r0 .. +3 of lane
+      // kk + 32*((c4 % 8) % 2), db = c4 / 8, r0 = 4*((c4 % 8) / 2).
+      const int kk = tid >> 4, c4 = tid & 15;
+      const int src_lane = kk + 32 * (c4 & 1);
+      const int f = 4 * (c4 >> 3) + ((c4 & 7) >> 1);
+      float4 sk = part[f * 64 + src_lane], sv = part[(8 + f) * 64 + src_lane];
 #pragma unroll
       for (int w = 1; w < NWAVES; ++w) {
-        const float4 x = *reinterpret_cast<const float4*>(part + (w * 64 + src_lane) * PART_STRIDE + r0);
-        sum.x += x.x;
-        sum.y += x.y;
-        sum.z += x.z;
-        sum.w += x.w;
+        const float4 xk = part[(w * 16 + f) * 64 + src_lane];
+        const float4 xv = part[(w * 16 + 8 + f) * 64 + src_lane];
+        sk.x += xk.x; sk.y += xk.y; sk.z += xk.z; sk.w += xk.w;
+        sv.x += xv.x; sv.y += xv.y; sv.z += xv.z; sv.w += xv.w;
       }
-      u32x2_t o2;
-      o2[0] = pack_bf16x2(sum.x * f, sum.y * f);
-      o2[1] = pack_bf16x2(sum.z * f, sum.w * f);
-      bstore8(out, out_off, o2);  // rows past the sequence end are dropped
-    };
-    reduce_store(dk_acc, rdk, scale);
-    reduce_store(dv_acc, rdv, 1.0f);
-    __syncthreads();  // partial buffer is reused as wave regions by the next block
+      const uint32_t out_off = (uint32_t)(k0 + kk) * kv_row + (uint32_t)kvh * kHeadDim * 2 + 8 * c4;
+      u32x2_t ok, ov;
+      ok[0] = pack_bf16x2(sk.x * scale, sk.y * scale);
+      ok[1] = pack_bf16x2(sk.z * scale, sk.w * scale);
+      ov[0] = pack_bf16x2(sv.x, sv.y);
+      ov[1] = pack_bf16x2(sv.z, sv.w);
+      bstore8(rdk, out_off, ok);  // rows past the sequence end are dropped
+      bstore8(rdv, out_off, ov);
+    }
+    __syncthreads();  // the partial buffer is reused by the next block
   }
 }
 
@@ -256,7 +263,7 @@ hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, 
 }
 
 const char* bwd_dkdv_tiles() {
-  return "dkdv_bf16{key_block=32,waves=8,pairs=(j,n-1-j),query_step=32,mfma=32x32x16,buffer_io}";
+  return "dkdv_bf16{key_block=32,waves=8,pairs=(j,n-1-j),query_step=32,mfma=32x32x16,lds_dma_x2}";
 }
 
 }  // namespace rca

@@ -126,6 +126,39 @@ __device__ __forceinline__ u32x4_t lds_operand_T(const uint16_t* tile, int pitch
   return o;
 }
 
+// Swizzled row-major tiles of 128-byte rows (64 bf16, no padding), as written by
+// load-to-LDS: 16-byte chunk c of row r is stored in slot c ^ swz(r) of that row,
+// swz(r) = 4*((r/2) % 2) + (r/4) % 4.  With 64 four-byte banks two consecutive
+// rows fill all banks, and this choice keeps both access patterns below free of
+// bank conflicts within each 32-lane half: a 16-byte read of one chunk from 16
+// consecutive rows, and the transposed reads of lds_operand_T_swz.
+__device__ __forceinline__ int swz_slot(int row, int chunk) {
+  return chunk ^ (4 * ((row >> 1) & 1) + ((row >> 2) & 3));
+}
+// Byte offset of element col (a multiple of 4) of row in a swizzled tile.
+__device__ __forceinline__ uint32_t swz_off(int row, int col) {
+  return (uint32_t)row * 128u + 16u * (uint32_t)swz_slot(row, col >> 3) + 2u * (uint32_t)(col & 7);
+}
+__device__ __forceinline__ u32x4_t lds_load16_swz(const uint16_t* tile, int row, int col) {
+  return *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(tile) + swz_off(row, col));
+}
+// lds_operand_T on a swizzled tile.
+__device__ __forceinline__ u32x4_t lds_operand_T_swz(const uint16_t* tile, int row0, int c0, int lane) {
+  const int grp = lane >> 4;
+  const int s = lane & 15;
+  const int row = row0 + 4 * (grp >> 1) + (s >> 2);
+  const int col = c0 + 16 * (grp & 1) + 4 * (s & 3);
+  const char* base = reinterpret_cast<const char*>(tile);
+  const u32x2_t lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(base + swz_off(row, col)));
+  const u32x2_t hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(base + swz_off(row + 8, col)));
+  u32x4_t o;
+  o[0] = lo[0];
+  o[1] = lo[1];
+  o[2] = hi[0];
+  o[3] = hi[1];
+  return o;
+}
+
 __device__ __forceinline__ u32x4_t zero4u() {
   u32x4_t z;
   z[0] = z[1] = z[2] = z[3] = 0u;
@@ -157,6 +190,34 @@ __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2_t v) {
 }
 __device__ __forceinline__ void bstore_f32(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+}
+
+// Load-to-LDS (measured on gfx950): buffer_load_dwordx4 ... lds writes lane i's
+// 16 bytes to LDS at M0 + 16*i; the scalar offset applies to the global address
+// only, and the wave's vmcnt covers the LDS write.  It is issued from inline
+// assembly so the compiler does not guard every later LDS read with a wait for
+// it (it cannot tell the destination apart from the buffers being read); the
+// kernels wait for these loads themselves with wait_loads().  The descriptor is
+// the raw four-dword form of make_rsrc's, in scalar registers.
+__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4_t r;
+  r[0] = (uint32_t)a;
+  r[1] = (uint32_t)(a >> 32) & 0xffffu;  // stride 0
+  r[2] = bytes;                           // range checked in bytes
+  r[3] = 0x00020000u;                     // the same flags make_rsrc uses
+  return r;
+}
+__device__ __forceinline__ void dma16(const u32x4_t& r, const void* lds, uint32_t off) {
+  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(lds));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0), "v"(off), "s"(r)
+      : "memory", "m0");
 }
 
 // Index of the calling wave within its workgroup, as a scalar (wave-uniform) value.
