@@ -30,8 +30,9 @@
 //     dV^T and dK^T with the transposed A operands read by ds_read_b64_tr_b16;
 //   * K and V of the key block are staged once through LDS and held in
 //     registers as the B operands of S and dP;
-//   * the eight partials are summed through LDS in wave order 0..7 and written
-//     once (dK scaled by the softmax scale), in bf16 with round to nearest even.
+//   * each wave parks its partial in its own LDS region; the eight partials are
+//     summed in wave order 0..7 and written once (dK scaled by the softmax
+//     scale), in bf16 with round to nearest even.
 #include "cdna4.hpp"
 #include "launch.hpp"
 
@@ -45,8 +46,7 @@ constexpr int BUF_BYTES = 2 * ROWS_BYTES + 256;        // q rows, dO rows, 64 ro
 constexpr int WAVE_BYTES = 2 * BUF_BYTES;              // double-buffered
 constexpr int KV_OFF = NWAVES * WAVE_BYTES;            // staging of the block's K and V rows
 constexpr int SMEM_BYTES = KV_OFF + 2 * ROWS_BYTES;
-constexpr int PART_BYTES = NWAVES * 16 * 64 * 16;      // [wave][16 float4 per lane][lane]
-static_assert(PART_BYTES <= SMEM_BYTES, "reduction buffer must fit");
+static_assert(16 * 64 * 16 <= WAVE_BYTES, "a wave's partial dK, dV must fit its region");
 static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
 
 __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
@@ -206,30 +206,36 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
     }
 
     // Sum the eight partials in wave order and write dK (scaled) and dV once.
-    // Partial layout: [wave][float4 index f][lane], f = 0..7 dK, 8..15 dV, float4
-    // f of a tensor being accumulator registers 4f .. 4f+3 of the flat 32.
-    __syncthreads();  // every wave is past its last step: the regions are free
-    float4* part = reinterpret_cast<float4*>(smem);
+    // Each wave stores its partial in its own region as soon as its last step
+    // is done: [float4 index f][lane], f = 0..7 dK, 8..15 dV, float4 f of a
+    // tensor being accumulator registers 4f .. 4f+3 of the flat 32.
+    {
+      float4* mine = reinterpret_cast<float4*>(my_region);
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const f32x16_t& a = dk_acc[f >> 2];
-      const f32x16_t& c = dv_acc[f >> 2];
-      const int r = 4 * (f & 3);
-      part[(wave * 16 + f) * 64 + lane] = make_float4(a[r], a[r + 1], a[r + 2], a[r + 3]);
-      part[(wave * 16 + 8 + f) * 64 + lane] = make_float4(c[r], c[r + 1], c[r + 2], c[r + 3]);
+      for (int f = 0; f < 8; ++f) {
+        const f32x16_t& a = dk_acc[f >> 2];
+        const f32x16_t& c = dv_acc[f >> 2];
+        const int r = 4 * (f & 3);
+        mine[f * 64 + lane] = make_float4(a[r], a[r + 1], a[r + 2], a[r + 3]);
+        mine[(8 + f) * 64 + lane] = make_float4(c[r], c[r + 1], c[r + 2], c[r + 3]);
+      }
     }
     __syncthreads();
     {
-      // Thread -> (key kk, d = 4*c4 .. 4*c4+3): registers 16*db + r0 .. +3 of lane
-      // kk + 32*((c4 % 8) % 2), db = c4 / 8, r0 = 4*((c4 % 8) / 2).
-      const int kk = tid >> 4, c4 = tid & 15;
-      const int src_lane = kk + 32 * (c4 & 1);
-      const int f = 4 * (c4 >> 3) + ((c4 & 7) >> 1);
-      float4 sk = part[f * 64 + src_lane], sv = part[(8 + f) * 64 + src_lane];
+      // Thread -> (key kk, d = 4*c4 .. 4*c4+3), which is registers 16*db + r0 .. +3
+      // of lane kk + 32*(c4 % 2) with db = c4 / 8, r0 = 4*((c4 % 8) / 2).  One wave
+      // covers the 64 lanes of one float4 index, so its LDS reads are consecutive.
+      const int src_lane = tid & 63;
+      const int kk = tid & 31;
+      const int c4 = 2 * wave + ((tid >> 5) & 1);
+      const int f = 4 * (c4 >> 3) + ((c4 & 7) >> 1);  // = 4*(wave/4) + wave%4
+      const float4* part0 = reinterpret_cast<const float4*>(smem);
+      float4 sk = part0[f * 64 + src_lane], sv = part0[(8 + f) * 64 + src_lane];
 #pragma unroll
       for (int w = 1; w < NWAVES; ++w) {
-        const float4 xk = part[(w * 16 + f) * 64 + src_lane];
-        const float4 xv = part[(w * 16 + 8 + f) * 64 + src_lane];
+        const float4* part = reinterpret_cast<const float4*>(smem + w * WAVE_BYTES);
+        const float4 xk = part[f * 64 + src_lane];
+        const float4 xv = part[(8 + f) * 64 + src_lane];
         sk.x += xk.x; sk.y += xk.y; sk.z += xk.z; sk.w += xk.w;
         sv.x += xv.x; sv.y += xv.y; sv.z += xv.z; sv.w += xv.w;
       }
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
       bstore8(rdk, out_off, ok);  // rows past the sequence end are dropped
       bstore8(rdv, out_off, ov);
     }
-    __syncthreads();  // the partial buffer is reused by the next block
+    __syncthreads();  // the regions are refilled by the next block
   }
 }
 
