@@ -89,6 +89,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
   // instruction's eight rows, i.e. it fetches chunk swz_slot(row, lane % 8).
   const int dma_row = lane >> 3;
   auto dma_chunk_bytes = [&](int row) { return 16u * (uint32_t)swz_slot(row, lane & 7); };
+  // Per-lane part of the source offset of instruction i of a step (row 8i + lane/8
+  // of the 32, chunk by the swizzle); the step's part is wave-uniform.
+  uint32_t row_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) row_off[i] = (uint32_t)(8 * i + dma_row) * q_row + dma_chunk_bytes(8 * i + dma_row);
 
   for (int half = 0; half < 2; ++half) {
     const int j = half == 0 ? pair : nkb - 1 - pair;
@@ -108,12 +113,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dkdv_bf16_kernel(
       const int qb = qb0 + (s - hh * per_head);
       const int h = kvh * G + hh;
       char* dst = my_region + buf * BUF_BYTES;
+      const uint32_t step_off = (uint32_t)(32 * qb) * q_row + (uint32_t)h * kHeadDim * 2;  // scalar
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 8 * i + dma_row;
-        const uint32_t off = (uint32_t)(32 * qb + r) * q_row + (uint32_t)h * kHeadDim * 2 + dma_chunk_bytes(r);
-        dma16(q_src, dst + 1024 * i, off);
-        dma16(do_src, dst + ROWS_BYTES + 1024 * i, off);
+        dma16s(q_src, dst + 1024 * i, row_off[i], step_off);
+        dma16s(do_src, dst + ROWS_BYTES + 1024 * i, row_off[i], step_off);
       }
       const uint32_t soff = ((uint32_t)h * T + 32 * qb + l32) * 4;
       l_raw = bload_f32(rl, soff);

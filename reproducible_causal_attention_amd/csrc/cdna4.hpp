@@ -219,6 +219,18 @@ __device__ __forceinline__ void dma16(const u32x4_t& r, const void* lds, uint32_
       : "s"(m0), "v"(off), "s"(r)
       : "memory", "m0");
 }
+// Same with a wave-uniform byte offset soff added to the global address.
+__device__ __forceinline__ void dma16s(const u32x4_t& r, const void* lds, uint32_t off, uint32_t soff) {
+  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(lds));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(m0), "v"(off), "s"(r), "s"(soff)
+      : "memory", "m0");
+}
 
 // Index of the calling wave within its workgroup, as a scalar (wave-uniform) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
