@@ -10,10 +10,11 @@
 // Decomposition (MI355X-first):
 //   * a workgroup of 8 waves owns 128 query rows of one (batch, query head):
 //     four 32-row query blocks times two key halves;
-//   * key/value tiles of 64 rows are staged row-major in LDS, double-buffered
-//     (the next tile's global loads are in flight while the current one is
-//     used); wave (query block qb, key half kh) uses keys 32*kh .. 32*kh+31 of
-//     each tile, so every K/V row in LDS feeds four waves;
+//   * key/value tiles of 64 rows go straight from HBM into double-buffered LDS
+//     (buffer_load ... lds, eight whole rows per instruction, XOR-swizzled
+//     16-byte chunks; the next tile's copy is in flight while the current one
+//     is used); wave (query block qb, key half kh) uses keys 32*kh .. 32*kh+31
+//     of each tile, so every K/V row in LDS feeds four waves;
 //   * S^T = K Q^T and dP^T = V dO^T put the queries on the lanes, so lse and
 //     delta are one register per lane, the dP accumulator starts at -delta
 //     (the MFMA adds dO.v to it), and dS^T feeds dQ^T += K^T dS^T directly from
@@ -27,21 +28,20 @@
 namespace rca {
 namespace {
 
-constexpr int PITCH = 72;
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per LDS tile
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int TILE = BN * PITCH;  // one K or V tile (bf16 elements)
-constexpr int PART_STRIDE = 36;
-static_assert(4 * 64 * PART_STRIDE * 4 <= 4 * TILE * 2, "reduction buffer must fit");
+constexpr int TILE_BYTES = BN * 128;  // one K or V tile: 64 swizzled rows of 64 bf16
+static_assert(4 * 8 * 64 * 16 <= 4 * TILE_BYTES, "reduction buffer must fit");
+static_assert(2 * BN * 8 == NWAVES * 64 * 2, "a tile pair is two load-to-LDS instructions per wave");
 
 __global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dq, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
     int causal) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -65,8 +65,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
   const uint32_t q_row = (uint32_t)Hq * kHeadDim * 2;   // bytes between tokens of q / o
   const uint32_t kv_row = (uint32_t)Hkv * kHeadDim * 2;  // bytes between tokens of k / v
   const size_t qe = (size_t)T * Hq * kHeadDim, ke = (size_t)T * Hkv * kHeadDim;
-  const rsrc_t rk = make_rsrc(k + b * ke, (uint32_t)T * kv_row);
-  const rsrc_t rv = make_rsrc(v + b * ke, (uint32_t)T * kv_row);
+  const u32x4_t k_src = raw_rsrc(k + b * ke, (uint32_t)T * kv_row);  // load-to-LDS sources
+  const u32x4_t v_src = raw_rsrc(v + b * ke, (uint32_t)T * kv_row);
 
   const int qw0 = qt * BM + 32 * qb;  // first query row of this wave
   const int my_q = qw0 + l32;
@@ -95,43 +95,40 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
   const int kv_end = causal ? min(T, (qt + 1) * BM) : T;
   const int n_kv = (kv_end + BN - 1) / BN;
 
-  // Tile staging: 64 rows x 8 chunks of 16 bytes for K and for V; one chunk of
-  // each per thread, a wave instruction covers 8 whole rows.
-  const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
-  const uint32_t ld_off = (uint32_t)ld_row * kv_row + (uint32_t)kvh * kHeadDim * 2 + 2 * ld_col;
-  u32x4_t kreg, vreg;
-  auto gload_tile = [&](int kt) {  // rows past the sequence end read as zero
-    const uint32_t off = ld_off + (uint32_t)(kt * BN) * kv_row;
-    kreg = bload16(rk, off);
-    vreg = bload16(rv, off);
-  };
-  auto store_tile = [&](int buf) {
-    lds_store16(smem + (2 * buf) * TILE + ld_row * PITCH + ld_col, kreg);
-    lds_store16(smem + (2 * buf + 1) * TILE + ld_row * PITCH + ld_col, vreg);
+  // Tile copy: wave w copies rows 8w .. 8w+7 of the K tile and of the V tile;
+  // lane fills slot lane % 8 of row 8w + lane / 8 (rows past the sequence end
+  // read as zero).
+  const int cp_row = 8 * wave + (lane >> 3);
+  const uint32_t cp_off = (uint32_t)cp_row * kv_row + (uint32_t)kvh * kHeadDim * 2 +
+                          16u * (uint32_t)swz_slot(cp_row, lane & 7);
+  auto copy_tile = [&](int kt, int buf) {
+    const uint32_t soff = (uint32_t)(kt * BN) * kv_row;  // scalar
+    char* dst = smem + (2 * buf) * TILE_BYTES + 1024 * wave;
+    dma16s(k_src, dst, cp_off, soff);
+    dma16s(v_src, dst + TILE_BYTES, cp_off, soff);
   };
 
-  gload_tile(0);  // in flight together with the row loads above
+  copy_tile(0, 0);  // in flight together with the row loads above
   wait_loads();
   const float L2 = lse_raw * kLog2e;
   f32x16_t neg_delta;
 #pragma unroll
   for (int r = 0; r < 16; ++r) neg_delta[r] = -Dl;
-  store_tile(0);
   __syncthreads();
 
   for (int kt = 0; kt < n_kv; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < n_kv) gload_tile(kt + 1);
-    const uint16_t* sK = smem + (2 * cur) * TILE;
-    const uint16_t* sV = smem + (2 * cur + 1) * TILE;
+    if (kt + 1 < n_kv) copy_tile(kt + 1, cur ^ 1);  // that buffer was last read before the previous barrier
+    const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + (2 * cur) * TILE_BYTES);
+    const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + (2 * cur + 1) * TILE_BYTES);
     const int kb0 = kt * BN + 32 * kh;  // first key of this wave's half
     const bool active = kb0 < T && (!causal || kb0 <= qw0 + 31);
     if (active) {
       f32x16_t sacc = zero16(), pacc = neg_delta;  // dP^T - delta accumulates from -delta
 #pragma unroll
       for (int s = 0; s < 4; ++s) {  // first product adds to a literal zero
-        const u32x4_t ak = lds_load16(sK + (32 * kh + l32) * PITCH + 16 * s + 8 * g);
-        const u32x4_t av = lds_load16(sV + (32 * kh + l32) * PITCH + 16 * s + 8 * g);
+        const u32x4_t ak = lds_load16_swz(sK, 32 * kh + l32, 16 * s + 8 * g);
+        const u32x4_t av = lds_load16_swz(sV, 32 * kh + l32, 16 * s + 8 * g);
         sacc = mfma_32x32x16(ak, qf[s], sacc);
         pacc = mfma_32x32x16(av, df[s], pacc);
       }
@@ -152,24 +149,25 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
       const u32x4_t ds0 = pack_operand(pacc, 0), ds1 = pack_operand(pacc, 8);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        dq_acc[db] = mfma_32x32x16(lds_operand_T(sK, PITCH, 32 * kh, 32 * db, lane), ds0, dq_acc[db]);
-        dq_acc[db] = mfma_32x32x16(lds_operand_T(sK, PITCH, 32 * kh + 16, 32 * db, lane), ds1, dq_acc[db]);
+        dq_acc[db] = mfma_32x32x16(lds_operand_T_swz(sK, 32 * kh, 32 * db, lane), ds0, dq_acc[db]);
+        dq_acc[db] = mfma_32x32x16(lds_operand_T_swz(sK, 32 * kh + 16, 32 * db, lane), ds1, dq_acc[db]);
       }
     }
-    if (kt + 1 < n_kv) store_tile(cur ^ 1);  // that buffer was last read before the previous barrier
+    wait_loads();  // the next tile has landed in LDS
     __syncthreads();
   }
 
-  // dQ = key half 0 + key half 1, in that order.
-  float* part = reinterpret_cast<float*>(smem);
-  float* slot = part + (qb * 64 + lane) * PART_STRIDE;
+  // dQ = key half 0 + key half 1, in that order.  Partial of half 1 in LDS as
+  // [query block][float4 index f = 4*db + j][lane] (consecutive lanes, no bank
+  // conflicts); the last tile's copy has landed and every wave is past its reads.
+  float4* part = reinterpret_cast<float4*>(smem) + qb * 8 * 64 + lane;
   if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 4)
-        *reinterpret_cast<float4*>(slot + 16 * db + r) =
-            make_float4(dq_acc[db][r], dq_acc[db][r + 1], dq_acc[db][r + 2], dq_acc[db][r + 3]);
+      for (int j = 0; j < 4; ++j)
+        part[(4 * db + j) * 64] = make_float4(dq_acc[db][4 * j], dq_acc[db][4 * j + 1],
+                                              dq_acc[db][4 * j + 2], dq_acc[db][4 * j + 3]);
     }
   }
   __syncthreads();
@@ -178,7 +176,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 x = *reinterpret_cast<const float4*>(slot + 16 * db + 4 * j);
+        const float4 x = part[(4 * db + j) * 64];
         u32x2_t w;
         w[0] = pack_bf16x2((dq_acc[db][4 * j + 0] + x.x) * scale, (dq_acc[db][4 * j + 1] + x.y) * scale);
         w[1] = pack_bf16x2((dq_acc[db][4 * j + 2] + x.z) * scale, (dq_acc[db][4 * j + 3] + x.w) * scale);
