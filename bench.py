@@ -81,6 +81,13 @@ def main() -> int:
                     help="also time a stack of this many independent layers (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle cpu_baseline sample (0: skip)")
+    ap.add_argument("--kernel-only", default=None,
+                    choices=("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"),
+                    help="counter runs: launch only this kernel --launches times and exit")
+    ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="counter calibration: copy this many bytes device to device "
+                         "--launches times and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -98,6 +105,17 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_bytes > 0:
+        # A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it
+        # calibrates the counters to bytes.
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.launches):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_bytes} bytes x {args.launches}")
+        return 0
     lib = A.load_library()
     w = W.WORKLOADS[args.workload]
     if w.dtype != "bf16":
@@ -159,6 +177,18 @@ def main() -> int:
         for n in ("o", "lse", "dq", "dk", "dv"):
             h.update(b[n].contiguous().view(torch.uint8).cpu().numpy().tobytes())
         return h.hexdigest()
+
+    if args.kernel_only:
+        # Counter runs: inputs and the forward's outputs in place, then only the
+        # named kernel.
+        bufs = buffers()
+        step((q, k, v, dO), bufs)
+        torch.cuda.synchronize()
+        for _ in range(args.launches):
+            kernel(args.kernel_only, (q, k, v, dO), bufs)
+        torch.cuda.synchronize()
+        log(f"{args.kernel_only} x {args.launches} on {w.name}")
+        return 0
 
     # ---- correctness gate (no oracle): finite, reproducible, invariants ----
     bufs = buffers()
