@@ -50,8 +50,10 @@
  * another output; a workspace smaller than attn_bwd_workspace_bytes(); sizes
  * beyond the limits below.  ATTN_ERR_UNSUPPORTED: D != 64 or an unknown dtype.
  * ATTN_ERR_HIP: the HIP runtime reported an error for a launch (the value of
- * hipGetLastError() after the launch).  Nothing aborts and no C++ exception
- * crosses the interface.
+ * hipGetLastError() after the launch; an error pending from an earlier,
+ * unrelated runtime call is discarded before the launch, so it is not reported
+ * as this call's failure).  Nothing aborts and no C++ exception crosses the
+ * interface.
  *
  * Limits: T <= 2^24; ceil(T/64)*B*Hq < 2^23; every tensor holds fewer than
  * 2^40 elements; and one batch element of q (T*Hq*D elements) spans fewer than

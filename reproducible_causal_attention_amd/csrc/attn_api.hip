@@ -90,6 +90,12 @@ rca::Problem make_problem(int B, int T, int Hq, int Hkv, float scale, int causal
 
 attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// hipGetLastError() returns the last error of any runtime call on this thread.
+// Called once before an entry point's launches, it discards an error left by an
+// earlier, unrelated call (which that call already returned to its caller), so
+// the status after the launch is the launch's own.
+void discard_stale_error() { (void)hipGetLastError(); }
+
 #define ATTN_TRY(expr)                       \
   do {                                       \
     const attn_status_t st_ = (expr);        \
@@ -109,6 +115,7 @@ ATTN_EXPORT attn_status_t attn_fwd(const void* q, const void* k, const void* v, 
   const size_t lb = (size_t)B * Hq * T * sizeof(float);
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb)},
                           {span_of(o, qb), span_of(lse, lb)}));
+  discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16 ? rca::launch_fwd_bf16(p, q, k, v, o, lse, s)
@@ -129,6 +136,7 @@ ATTN_EXPORT attn_status_t attn_bwd_preprocess(const void* o, const void* dO, flo
   const size_t qb = (size_t)B * T * Hq * D * elem_size(dtype);
   const size_t lb = (size_t)B * Hq * T * sizeof(float);
   ATTN_TRY(check_disjoint({span_of(o, qb), span_of(dO, qb)}, {span_of(delta, lb)}));
+  discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hq, 1.0f, 1);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16 ? rca::launch_bwd_pre_bf16(p, o, dO, delta, s)
@@ -148,6 +156,7 @@ ATTN_EXPORT attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(dO, qb),
                            span_of(lse, lb), span_of(delta, lb)},
                           {span_of(dk, kb), span_of(dv, kb)}));
+  discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16
@@ -168,6 +177,7 @@ ATTN_EXPORT attn_status_t attn_bwd_dq(const void* q, const void* k, const void* 
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(dO, qb),
                            span_of(lse, lb), span_of(delta, lb)},
                           {span_of(dq, qb)}));
+  discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16 ? rca::launch_bwd_dq_bf16(p, q, k, v, dO, lse, delta, dq, s)
@@ -192,6 +202,7 @@ ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, 
                           {span_of(dq, qb), span_of(dk, kb), span_of(dv, kb),
                            span_of(workspace, need)}));
   float* delta = static_cast<float*>(workspace);
+  discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16) {
