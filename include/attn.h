@@ -96,9 +96,10 @@ size_t attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D, attn_dtype
 
 /* Backward of sum(o * dO).  o and lse must be the outputs of attn_fwd for the
  * same q, k, v, scale and causal.  Enqueues, in order, attn_bwd_preprocess
- * (delta into the workspace), attn_bwd_dkdv and attn_bwd_dq.  dq, dk, dv must
- * not overlap any input, the workspace or each other; the workspace must hold
- * at least attn_bwd_workspace_bytes() bytes and is clobbered. */
+ * (delta into the workspace) and attn_bwd_dkdv_dq; the results are bitwise those
+ * of attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq called in turn.  dq, dk,
+ * dv must not overlap any input, the workspace or each other; the workspace must
+ * hold at least attn_bwd_workspace_bytes() bytes and is clobbered. */
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
                        int B, int T, int Hq, int Hkv, int D, float scale, int causal,
@@ -128,6 +129,17 @@ attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const voi
                           const float* lse, const float* delta, void* dq,
                           int B, int T, int Hq, int Hkv, int D, float scale, int causal,
                           attn_dtype_t dtype, void* stream);
+
+/* Backward steps 2 and 3 co-launched in one grid (they are independent once
+ * delta is known): the dQ units of attn_bwd_dq, heaviest first, then the dK/dV
+ * units of attn_bwd_dkdv, so a CU that finishes a short dQ tile takes dK/dV work
+ * instead of waiting for a second launch.  dq, dk and dv are bitwise those of
+ * the two separate calls.  Arguments as there; dq, dk, dv must not overlap any
+ * input or each other. */
+attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dO,
+                               const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                               int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                               attn_dtype_t dtype, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status_t status);

@@ -23,7 +23,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = (
     "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-    "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string", "attn_build_info",
+    "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dkdv_dq", "attn_status_string", "attn_build_info",
 )
 
 _lib = None
@@ -59,7 +59,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_preprocess.argtypes = [P, P, P, I, I, I, I, I, P]
     lib.attn_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, P, *sizes, F, I, I, P]
     lib.attn_bwd_dq.argtypes = [P, P, P, P, P, P, P, *sizes, F, I, I, P]
-    for name in ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"):
+    lib.attn_bwd_dkdv_dq.argtypes = [P, P, P, P, P, P, P, P, P, *sizes, F, I, I, P]
+    for name in ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
+                 "attn_bwd_dkdv_dq"):
         getattr(lib, name).restype = I
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -173,3 +175,16 @@ def bwd_dq(q, k, v, dO, lse, delta, scale=None, causal=True):
                            _ptr(dq), B, T, Hq, Hkv, D, scale, int(bool(causal)),
                            _dtype_code(q), _stream()))
     return dq
+
+
+def bwd_dkdv_dq(q, k, v, dO, lse, delta, scale=None, causal=True):
+    """dK/dV and dQ co-launched in one grid: returns ``(dq, dk, dv)``, bitwise those
+    of ``bwd_dkdv`` and ``bwd_dq``."""
+    lib = load_library()
+    B, T, Hq, Hkv, D = _shapes(q, k)
+    scale = default_scale(D) if scale is None else float(scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib.attn_bwd_dkdv_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
+                                _ptr(dq), _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale,
+                                int(bool(causal)), _dtype_code(q), _stream()))
+    return dq, dk, dv

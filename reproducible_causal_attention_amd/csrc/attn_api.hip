@@ -207,10 +207,32 @@ ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16) {
     ATTN_TRY(from_hip(rca::launch_bwd_pre_bf16(p, o, dO, delta, s)));
-    ATTN_TRY(from_hip(rca::launch_bwd_dkdv_bf16(p, q, k, v, dO, lse, delta, dk, dv, s)));
-    return from_hip(rca::launch_bwd_dq_bf16(p, q, k, v, dO, lse, delta, dq, s));
+    return from_hip(rca::launch_bwd_dkdv_dq_bf16(p, q, k, v, dO, lse, delta, dq, dk, dv, s));
   }
   ATTN_TRY(from_hip(rca::launch_bwd_pre_f32(p, o, dO, delta, s)));
+  ATTN_TRY(from_hip(rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s)));
+  return from_hip(rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
+}
+
+ATTN_EXPORT attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const void* v,
+                                           const void* dO, const float* lse, const float* delta,
+                                           void* dq, void* dk, void* dv, int B, int T, int Hq,
+                                           int Hkv, int D, float scale, int causal,
+                                           attn_dtype_t dtype, void* stream) {
+  ATTN_TRY(check_ptrs({q, k, v, dO, lse, delta, dq, dk, dv}));
+  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_scalars(scale, causal));
+  const size_t es = elem_size(dtype);
+  const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
+  const size_t lb = (size_t)B * Hq * T * sizeof(float);
+  ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(dO, qb),
+                           span_of(lse, lb), span_of(delta, lb)},
+                          {span_of(dq, qb), span_of(dk, kb), span_of(dv, kb)}));
+  discard_stale_error();
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16)
+    return from_hip(rca::launch_bwd_dkdv_dq_bf16(p, q, k, v, dO, lse, delta, dq, dk, dv, s));
   ATTN_TRY(from_hip(rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s)));
   return from_hip(rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
 }

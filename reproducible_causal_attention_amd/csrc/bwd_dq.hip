@@ -1,189 +1,18 @@
-// bwd_dq.hip -- dQ of fused causal attention, bf16 on gfx950 MFMA.
-//
-// For a block of query rows, recompute P from the saved log-sum-exp (the
-// causal_probs_from_lse step of "Training a 100M transformer in pure Rust:
-// RustingBrain vs PyTorch and TensorFlow", section "Step 1: measure before
-// changing anything"), form dS = P * (dP - delta) and accumulate
-// dQ = scale * sum_j dS_ij k_j over the keys the rows can see.  dQ has one owner
-// per row, so there are no atomics and the sum order is fixed.
-//
-// Decomposition (MI355X-first):
-//   * a workgroup of 8 waves owns 128 query rows of one (batch, query head):
-//     four 32-row query blocks times two key halves;
-//   * key/value tiles of 64 rows go straight from HBM into double-buffered LDS
-//     (buffer_load ... lds, eight whole rows per instruction, XOR-swizzled
-//     16-byte chunks; the next tile's copy is in flight while the current one
-//     is used); wave (query block qb, key half kh) uses keys 32*kh .. 32*kh+31
-//     of each tile, so every K/V row in LDS feeds four waves;
-//   * S^T = K Q^T and dP^T = V dO^T put the queries on the lanes, so lse and
-//     delta are one register per lane, the dP accumulator starts at -delta
-//     (the MFMA adds dO.v to it), and dS^T feeds dQ^T += K^T dS^T directly from
-//     the accumulators with K^T read by ds_read_b64_tr_b16;
-//   * the two key halves' fp32 partials are added in a fixed order through LDS;
-//   * query tiles are issued heaviest first, and the tiles of one
-//     (batch, KV head) group run on one XCD so they share its L2.
-#include "cdna4.hpp"
-#include "launch.hpp"
+// bwd_dq.hip -- launcher of the dQ kernel (a4); the work of one unit is in
+// dq_body.hpp.
+#include "dq_body.hpp"
 
 namespace rca {
 namespace {
 
-constexpr int BM = 128;  // query rows per workgroup
-constexpr int BN = 64;   // keys per LDS tile
-constexpr int NWAVES = 8;
-constexpr int NTHREADS = NWAVES * 64;
-constexpr int TILE_BYTES = BN * 128;  // one K or V tile: 64 swizzled rows of 64 bf16
-static_assert(4 * 8 * 64 * 16 <= 4 * TILE_BYTES, "reduction buffer must fit");
-static_assert(2 * BN * 8 == NWAVES * 64 * 2, "a tile pair is two load-to-LDS instructions per wave");
-
-__global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
+__global__ __launch_bounds__(dqb::NTHREADS) void attn_bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dq, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
     int causal) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];  // [buffer][K, V]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_id();
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-  const int qb = wave & 3;   // query block within the tile
-  const int kh = wave >> 2;  // key half within each K/V tile
-
-  const int G = Hq / Hkv;
-  const int n_qt = (T + BM - 1) / BM;
-  int gi, rank;
-  decode_unit(blockIdx.x, B * Hkv, gi, rank);
-  const int b = gi / Hkv;
-  const int kvh = gi - b * Hkv;
-  const int hh = rank % G;
-  const int qt = causal ? n_qt - 1 - rank / G : rank / G;  // heaviest tiles first
-  const int h = kvh * G + hh;
-
-  // Per-batch-element buffers; byte offsets below are within one batch element.
-  const uint32_t q_row = (uint32_t)Hq * kHeadDim * 2;   // bytes between tokens of q / o
-  const uint32_t kv_row = (uint32_t)Hkv * kHeadDim * 2;  // bytes between tokens of k / v
-  const size_t qe = (size_t)T * Hq * kHeadDim, ke = (size_t)T * Hkv * kHeadDim;
-  const u32x4_t k_src = raw_rsrc(k + b * ke, (uint32_t)T * kv_row);  // load-to-LDS sources
-  const u32x4_t v_src = raw_rsrc(v + b * ke, (uint32_t)T * kv_row);
-
-  const int qw0 = qt * BM + 32 * qb;  // first query row of this wave
-  const int my_q = qw0 + l32;
-  const uint32_t qoff = (uint32_t)my_q * q_row + (uint32_t)h * kHeadDim * 2;  // bytes
-
-  // Q^T and dO^T as B operands (queries on the lanes).
-  const rsrc_t rq = make_rsrc(q + b * qe, (uint32_t)T * q_row);
-  const rsrc_t rdo = make_rsrc(dO + b * qe, (uint32_t)T * q_row);
-  const rsrc_t rdq = make_rsrc(dq + b * qe, (uint32_t)T * q_row);
-  u32x4_t qf[4], df[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    qf[s] = bload16(rq, qoff + 32 * s + 16 * g);
-    df[s] = bload16(rdo, qoff + 32 * s + 16 * g);
-  }
-  // Rows past the sequence end read lse = delta = 0 (buffer range check) and are
-  // never stored.
-  const rsrc_t rl = make_rsrc(lse + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
-  const rsrc_t rdl = make_rsrc(delta + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
-  const uint32_t stat_off = ((uint32_t)h * T + my_q) * 4;
-  const float lse_raw = bload_f32(rl, my_q < T ? stat_off : 0xffffffffu);
-  const float Dl = bload_f32(rdl, my_q < T ? stat_off : 0xffffffffu);
-
-  f32x16_t dq_acc[2] = {zero16(), zero16()};  // dQ^T: rows d = 32*db + 8*(r/4) + 4g + r%4
-
-  const int kv_end = causal ? min(T, (qt + 1) * BM) : T;
-  const int n_kv = (kv_end + BN - 1) / BN;
-
-  // Tile copy: wave w copies rows 8w .. 8w+7 of the K tile and of the V tile;
-  // lane fills slot lane % 8 of row 8w + lane / 8 (rows past the sequence end
-  // read as zero).
-  const int cp_row = 8 * wave + (lane >> 3);
-  const uint32_t cp_off = (uint32_t)cp_row * kv_row + (uint32_t)kvh * kHeadDim * 2 +
-                          16u * (uint32_t)swz_slot(cp_row, lane & 7);
-  auto copy_tile = [&](int kt, int buf) {
-    const uint32_t soff = (uint32_t)(kt * BN) * kv_row;  // scalar
-    char* dst = smem + (2 * buf) * TILE_BYTES + 1024 * wave;
-    dma16s(k_src, dst, cp_off, soff);
-    dma16s(v_src, dst + TILE_BYTES, cp_off, soff);
-  };
-
-  copy_tile(0, 0);  // in flight together with the row loads above
-  wait_loads();
-  const float L2 = lse_raw * kLog2e;
-  f32x16_t neg_delta;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) neg_delta[r] = -Dl;
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kv; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < n_kv) copy_tile(kt + 1, cur ^ 1);  // that buffer was last read before the previous barrier
-    const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + (2 * cur) * TILE_BYTES);
-    const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + (2 * cur + 1) * TILE_BYTES);
-    const int kb0 = kt * BN + 32 * kh;  // first key of this wave's half
-    const bool active = kb0 < T && (!causal || kb0 <= qw0 + 31);
-    if (active) {
-      f32x16_t sacc = zero16(), pacc = neg_delta;  // dP^T - delta accumulates from -delta
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {  // first product adds to a literal zero
-        const u32x4_t ak = lds_load16_swz(sK, 32 * kh + l32, 16 * s + 8 * g);
-        const u32x4_t av = lds_load16_swz(sV, 32 * kh + l32, 16 * s + 8 * g);
-        sacc = mfma_32x32x16(ak, qf[s], sacc);
-        pacc = mfma_32x32x16(av, df[s], pacc);
-      }
-      // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.
-      if ((causal && kb0 + 31 > qw0) || kb0 + 32 > T) {
-        // Diagonal tile or sequence tail: zero P where the key is after the
-        // query or past the end.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const float p = fast_exp2(fmaf(sacc[r], scale_log2, -L2));
-          pacc[r] *= ((causal && key > my_q) || key >= T) ? 0.f : p;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pacc[r] *= fast_exp2(fmaf(sacc[r], scale_log2, -L2));
-      }
-      const u32x4_t ds0 = pack_operand(pacc, 0), ds1 = pack_operand(pacc, 8);
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        dq_acc[db] = mfma_32x32x16(lds_operand_T_swz(sK, 32 * kh, 32 * db, lane), ds0, dq_acc[db]);
-        dq_acc[db] = mfma_32x32x16(lds_operand_T_swz(sK, 32 * kh + 16, 32 * db, lane), ds1, dq_acc[db]);
-      }
-    }
-    wait_loads();  // the next tile has landed in LDS
-    __syncthreads();
-  }
-
-  // dQ = key half 0 + key half 1, in that order.  Partial of half 1 in LDS as
-  // [query block][float4 index f = 4*db + j][lane] (consecutive lanes, no bank
-  // conflicts); the last tile's copy has landed and every wave is past its reads.
-  float4* part = reinterpret_cast<float4*>(smem) + qb * 8 * 64 + lane;
-  if (kh == 1) {
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        part[(4 * db + j) * 64] = make_float4(dq_acc[db][4 * j], dq_acc[db][4 * j + 1],
-                                              dq_acc[db][4 * j + 2], dq_acc[db][4 * j + 3]);
-    }
-  }
-  __syncthreads();
-  if (kh == 0) {  // rows past the sequence end are dropped by the buffer range check
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 x = part[(4 * db + j) * 64];
-        u32x2_t w;
-        w[0] = pack_bf16x2((dq_acc[db][4 * j + 0] + x.x) * scale, (dq_acc[db][4 * j + 1] + x.y) * scale);
-        w[1] = pack_bf16x2((dq_acc[db][4 * j + 2] + x.z) * scale, (dq_acc[db][4 * j + 3] + x.w) * scale);
-        bstore8(rdq, qoff + 2 * (32 * db + 8 * j + 4 * g), w);
-      }
-    }
-  }
+  __shared__ __attribute__((aligned(16))) char smem[dqb::SMEM_BYTES];
+  dqb::unit_body(smem, blockIdx.x, q, k, v, dO, lse, delta, dq, B, T, Hq, Hkv, scale, scale_log2,
+                 causal);
 }
 
 }  // namespace
@@ -191,9 +20,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_bwd_dq_bf16_kernel(
 hipError_t launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
                               const void* dO, const float* lse, const float* delta, void* dq,
                               hipStream_t s) {
-  const int n_qt = (p.T + BM - 1) / BM;
+  const int n_qt = (p.T + dqb::BM - 1) / dqb::BM;
   const dim3 grid((unsigned)(n_qt * p.B * p.Hq));
-  attn_bwd_dq_bf16_kernel<<<grid, NTHREADS, 0, s>>>(
+  attn_bwd_dq_bf16_kernel<<<grid, dqb::NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta,
       static_cast<uint16_t*>(dq), p.B, p.T, p.Hq, p.Hkv, p.scale, p.scale_log2, p.causal);

@@ -161,6 +161,25 @@ def test_step_entry_points_validate(lib):
     assert lib.attn_bwd_dq(BASE, BASE + 16 * MB, BASE + 32 * MB, BASE + 48 * MB, BASE + 64 * MB,
                            BASE + 80 * MB, BASE + 96 * MB, 1, 128, 4, 2, 64, 0.125, -1,
                            A.ATTN_BF16, None) == A.ATTN_ERR_INVALID_ARG
+    # dkdv_dq: dq overlapping dk
+    assert lib.attn_bwd_dkdv_dq(BASE, BASE + 16 * MB, BASE + 32 * MB, BASE + 48 * MB,
+                                BASE + 64 * MB, BASE + 80 * MB, BASE + 96 * MB,
+                                BASE + 96 * MB + 64, BASE + 112 * MB, 1, 128, 4, 2, 64, 0.125, 1,
+                                A.ATTN_BF16, None) == A.ATTN_ERR_INVALID_ARG
+    # dkdv_dq: dv overlapping an input (delta)
+    assert lib.attn_bwd_dkdv_dq(BASE, BASE + 16 * MB, BASE + 32 * MB, BASE + 48 * MB,
+                                BASE + 64 * MB, BASE + 80 * MB, BASE + 96 * MB, BASE + 112 * MB,
+                                BASE + 80 * MB, 1, 128, 4, 2, 64, 0.125, 1,
+                                A.ATTN_BF16, None) == A.ATTN_ERR_INVALID_ARG
+    # dkdv_dq: null dv, Hq not a multiple of Hkv
+    assert lib.attn_bwd_dkdv_dq(BASE, BASE + 16 * MB, BASE + 32 * MB, BASE + 48 * MB,
+                                BASE + 64 * MB, BASE + 80 * MB, BASE + 96 * MB, BASE + 112 * MB,
+                                None, 1, 128, 4, 2, 64, 0.125, 1,
+                                A.ATTN_BF16, None) == A.ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd_dkdv_dq(BASE, BASE + 16 * MB, BASE + 32 * MB, BASE + 48 * MB,
+                                BASE + 64 * MB, BASE + 80 * MB, BASE + 96 * MB, BASE + 112 * MB,
+                                BASE + 128 * MB, 1, 128, 4, 3, 64, 0.125, 1,
+                                A.ATTN_BF16, None) == A.ATTN_ERR_INVALID_ARG
 
 
 def test_binding_refuses_cpu_tensors():

@@ -108,3 +108,38 @@ def test_steps_compose_to_bwd():
     dq2 = A.bwd_dq(q, k, v, dO, lse, delta, w.scale, True)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+@pytest.mark.parametrize("name", ["gqa-1x512", "tiny-f32", "gqa-4x1024"])
+def test_colaunched_backward_equals_two_launches(name):
+    """dK/dV and dQ in one grid give bitwise the results of the two launches."""
+    w = W.WORKLOADS[name]
+    inp = W.generate(w)
+    q, k, v, dO = to_device(inp)
+    say("co-launched backward", w.label())
+    o, lse = A.fwd(q, k, v, w.scale, True)
+    delta = A.bwd_preprocess(o, dO)
+    dq, dk, dv = A.bwd_dkdv_dq(q, k, v, dO, lse, delta, w.scale, True)
+    dk2, dv2 = A.bwd_dkdv(q, k, v, dO, lse, delta, w.scale, True)
+    dq2 = A.bwd_dq(q, k, v, dO, lse, delta, w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+@pytest.mark.parametrize("shape", [(3, 333, 6, 2), (1, 65, 12, 4), (2, 200, 4, 4)])
+def test_colaunched_backward_odd_grids(shape):
+    """Odd unit counts: the dQ part not a multiple of 8 (padding workgroups), odd
+    key-block counts (a middle block), non-causal."""
+    B, T, Hq, Hkv = shape
+    w = W.custom(B, T, Hq, Hkv, 64, "bf16", seed=41 + T)
+    inp = W.generate(w)
+    q, k, v, dO = to_device(inp)
+    for causal in (True, False):
+        say("co-launched backward", w.label(), "causal" if causal else "full")
+        o, lse = A.fwd(q, k, v, w.scale, causal)
+        delta = A.bwd_preprocess(o, dO)
+        dq, dk, dv = A.bwd_dkdv_dq(q, k, v, dO, lse, delta, w.scale, causal)
+        dk2, dv2 = A.bwd_dkdv(q, k, v, dO, lse, delta, w.scale, causal)
+        dq2 = A.bwd_dq(q, k, v, dO, lse, delta, w.scale, causal)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
