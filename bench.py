@@ -120,15 +120,16 @@ def main() -> int:
         return 0
     lib = A.load_library()
     w = W.WORKLOADS[args.workload]
-    if w.dtype != "bf16":
-        print("bench.py times bf16 workloads", file=sys.stderr)
+    if w.dtype not in ("bf16", "f16"):
+        print("bench.py times bf16 and f16 workloads", file=sys.stderr)
         return 2
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
     B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
     dev = torch.device("cuda:0")
     log("workload", w.name, w.label(), "|", lib.attn_build_info().decode())
 
     inp = W.generate(w)
-    q, k, v, dO = (torch.from_numpy(getattr(inp, n).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, dO = (torch.from_numpy(getattr(inp, n).view(np.int16)).view(tdt).to(dev)
                    for n in ("q", "k", "v", "dO"))
 
     def buffers():
@@ -138,7 +139,7 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
-    bf = A.ATTN_BF16
+    bf = A.ATTN_BF16 if w.dtype == "bf16" else A.ATTN_F16
     causal = int(w.causal)
 
     def launch(fn_name, *a):
@@ -294,10 +295,10 @@ def main() -> int:
     layers = None
     if args.layers > 0:
         L = args.layers
-        xs = [(torch.randn_like(q, dtype=torch.float32).to(torch.bfloat16),
-               torch.randn_like(k, dtype=torch.float32).to(torch.bfloat16),
-               torch.randn_like(v, dtype=torch.float32).to(torch.bfloat16),
-               torch.randn_like(dO, dtype=torch.float32).to(torch.bfloat16)) for _ in range(L)]
+        xs = [(torch.randn_like(q, dtype=torch.float32).to(tdt),
+               torch.randn_like(k, dtype=torch.float32).to(tdt),
+               torch.randn_like(v, dtype=torch.float32).to(tdt),
+               torch.randn_like(dO, dtype=torch.float32).to(tdt)) for _ in range(L)]
         bs = [buffers() for _ in range(L)]
 
         def stack_step():
@@ -350,7 +351,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D,
                    "causal": bool(w.causal), "scale": w.scale,

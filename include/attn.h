@@ -77,8 +77,10 @@ typedef enum {
 
 typedef enum {
   ATTN_F32 = 0,  /* float32 inputs and outputs, float32 arithmetic throughout   */
-  ATTN_BF16 = 1  /* bfloat16 inputs and outputs; bf16 matrix products with fp32
+  ATTN_BF16 = 1, /* bfloat16 inputs and outputs; bf16 matrix products with fp32
                     accumulation, fp32 softmax statistics, lse and delta        */
+  ATTN_F16 = 2   /* float16 inputs and outputs, otherwise as ATTN_BF16 (the same
+                    kernels with fp16 matrix products and conversions)           */
 } attn_dtype_t;
 
 /* Forward.  Reads q, k, v; writes o and lse (the per-row log-sum-exp that the

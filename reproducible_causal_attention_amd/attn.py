@@ -6,7 +6,7 @@ stream (``torch.cuda.current_stream()``).  If the library is missing the calls
 raise; there is no fallback.
 
 Layouts: q, o, dO, dq are [B, T, Hq, 64]; k, v, dk, dv are [B, T, Hkv, 64]
-(contiguous, bfloat16 or float32); lse and delta are [B, Hq, T] float32.
+(contiguous, bfloat16, float16 or float32); lse and delta are [B, Hq, T] float32.
 """
 from __future__ import annotations
 
@@ -19,7 +19,7 @@ import torch
 from . import build as _build
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 
 EXPORTED = (
     "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
@@ -85,9 +85,11 @@ def _check(status: int):
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_F16
     if t.dtype == torch.float32:
         return ATTN_F32
-    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16, torch.float16 or torch.float32")
 
 
 def _ptr(t: torch.Tensor) -> int:

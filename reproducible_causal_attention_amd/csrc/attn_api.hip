@@ -46,7 +46,7 @@ attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dty
   if (tiles >= kMaxTiles) return ATTN_ERR_INVALID_ARG;
   if ((long long)B * T * Hq * (long long)D >= kMaxElements) return ATTN_ERR_INVALID_ARG;
   if ((long long)T * Hq * (long long)D * 4 >= kMaxBatchBytes) return ATTN_ERR_INVALID_ARG;
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
   if (D != rca::kHeadDim) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
@@ -118,8 +118,9 @@ ATTN_EXPORT attn_status_t attn_fwd(const void* q, const void* k, const void* v, 
   discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(dtype == ATTN_BF16 ? rca::launch_fwd_bf16(p, q, k, v, o, lse, s)
-                                     : rca::launch_fwd_f32(p, q, k, v, o, lse, s));
+  return from_hip(dtype == ATTN_BF16  ? rca::launch_fwd_bf16(p, q, k, v, o, lse, s)
+                  : dtype == ATTN_F16 ? rca::launch_fwd_f16(p, q, k, v, o, lse, s)
+                                      : rca::launch_fwd_f32(p, q, k, v, o, lse, s));
 }
 
 ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype) {
@@ -139,8 +140,9 @@ ATTN_EXPORT attn_status_t attn_bwd_preprocess(const void* o, const void* dO, flo
   discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hq, 1.0f, 1);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(dtype == ATTN_BF16 ? rca::launch_bwd_pre_bf16(p, o, dO, delta, s)
-                                     : rca::launch_bwd_pre_f32(p, o, dO, delta, s));
+  return from_hip(dtype == ATTN_BF16  ? rca::launch_bwd_pre_bf16(p, o, dO, delta, s)
+                  : dtype == ATTN_F16 ? rca::launch_bwd_pre_f16(p, o, dO, delta, s)
+                                      : rca::launch_bwd_pre_f32(p, o, dO, delta, s));
 }
 
 ATTN_EXPORT attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
@@ -159,9 +161,9 @@ ATTN_EXPORT attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void
   discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(dtype == ATTN_BF16
-                      ? rca::launch_bwd_dkdv_bf16(p, q, k, v, dO, lse, delta, dk, dv, s)
-                      : rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s));
+  return from_hip(dtype == ATTN_BF16  ? rca::launch_bwd_dkdv_bf16(p, q, k, v, dO, lse, delta, dk, dv, s)
+                  : dtype == ATTN_F16 ? rca::launch_bwd_dkdv_f16(p, q, k, v, dO, lse, delta, dk, dv, s)
+                                      : rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s));
 }
 
 ATTN_EXPORT attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
@@ -180,8 +182,9 @@ ATTN_EXPORT attn_status_t attn_bwd_dq(const void* q, const void* k, const void* 
   discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(dtype == ATTN_BF16 ? rca::launch_bwd_dq_bf16(p, q, k, v, dO, lse, delta, dq, s)
-                                     : rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
+  return from_hip(dtype == ATTN_BF16  ? rca::launch_bwd_dq_bf16(p, q, k, v, dO, lse, delta, dq, s)
+                  : dtype == ATTN_F16 ? rca::launch_bwd_dq_f16(p, q, k, v, dO, lse, delta, dq, s)
+                                      : rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
 }
 
 ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -209,6 +212,10 @@ ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, 
     ATTN_TRY(from_hip(rca::launch_bwd_pre_bf16(p, o, dO, delta, s)));
     return from_hip(rca::launch_bwd_dkdv_dq_bf16(p, q, k, v, dO, lse, delta, dq, dk, dv, s));
   }
+  if (dtype == ATTN_F16) {
+    ATTN_TRY(from_hip(rca::launch_bwd_pre_f16(p, o, dO, delta, s)));
+    return from_hip(rca::launch_bwd_dkdv_dq_f16(p, q, k, v, dO, lse, delta, dq, dk, dv, s));
+  }
   ATTN_TRY(from_hip(rca::launch_bwd_pre_f32(p, o, dO, delta, s)));
   ATTN_TRY(from_hip(rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s)));
   return from_hip(rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
@@ -233,6 +240,8 @@ ATTN_EXPORT attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const v
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16)
     return from_hip(rca::launch_bwd_dkdv_dq_bf16(p, q, k, v, dO, lse, delta, dq, dk, dv, s));
+  if (dtype == ATTN_F16)
+    return from_hip(rca::launch_bwd_dkdv_dq_f16(p, q, k, v, dO, lse, delta, dq, dk, dv, s));
   ATTN_TRY(from_hip(rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s)));
   return from_hip(rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
 }

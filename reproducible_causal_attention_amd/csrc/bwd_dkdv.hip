@@ -5,30 +5,44 @@
 namespace rca {
 namespace {
 
-__global__ __launch_bounds__(dkdv::NTHREADS) void attn_bwd_dkdv_bf16_kernel(
+template <class E>
+__global__ __launch_bounds__(dkdv::NTHREADS) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
     float scale, float scale_log2, int causal) {
   __shared__ __attribute__((aligned(16))) char smem[dkdv::SMEM_BYTES];
-  dkdv::unit_body(smem, blockIdx.x, q, k, v, dO, lse, delta, dk, dv, B, T, Hq, Hkv, scale,
+  dkdv::unit_body<E>(smem, blockIdx.x, q, k, v, dO, lse, delta, dk, dv, B, T, Hq, Hkv, scale,
                   scale_log2, causal);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+template <class E>
+hipError_t launch_bwd_dkdv_e(const Problem& p, const void* q, const void* k, const void* v,
                                 const void* dO, const float* lse, const float* delta, void* dk,
                                 void* dv, hipStream_t s) {
   const int nkb = (p.T + 31) / 32;
   const int npairs = (nkb + 1) / 2;
   const dim3 grid((unsigned)(npairs * p.B * p.Hkv));
-  attn_bwd_dkdv_bf16_kernel<<<grid, dkdv::NTHREADS, 0, s>>>(
+  attn_bwd_dkdv_kernel<E><<<grid, dkdv::NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta,
       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), p.B, p.T, p.Hq, p.Hkv, p.scale,
       p.scale_log2, p.causal);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                const void* dO, const float* lse, const float* delta, void* dk,
+                                void* dv, hipStream_t s) {
+  return launch_bwd_dkdv_e<Bf16>(p, q, k, v, dO, lse, delta, dk, dv, s);
+}
+
+hipError_t launch_bwd_dkdv_f16(const Problem& p, const void* q, const void* k, const void* v,
+                                const void* dO, const float* lse, const float* delta, void* dk,
+                                void* dv, hipStream_t s) {
+  return launch_bwd_dkdv_e<F16>(p, q, k, v, dO, lse, delta, dk, dv, s);
 }
 
 const char* bwd_dkdv_tiles() {

@@ -17,7 +17,8 @@ namespace {
 constexpr int PRE_THREADS = 256;
 constexpr int PRE_ROWS = PRE_THREADS / 8;  // 8 lanes x 8 elements per 64-wide row
 
-__global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_bf16_kernel(
+template <class E>
+__global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO, float* __restrict__ delta,
     int T, int Hq, long long n_rows) {
   const long long row = (long long)blockIdx.x * PRE_ROWS + (threadIdx.x >> 3);
@@ -28,8 +29,8 @@ __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_bf16_kernel(
     const u32x4_t c = gload16(dO + row * kHeadDim + part * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc = fmaf(bf16_lo(a[i]), bf16_lo(c[i]), acc);
-      acc = fmaf(bf16_hi(a[i]), bf16_hi(c[i]), acc);
+      acc = fmaf(E::lo(a[i]), E::lo(c[i]), acc);
+      acc = fmaf(E::hi(a[i]), E::hi(c[i]), acc);
     }
   }
   // Fixed butterfly over the 8 lanes of the row.
@@ -48,13 +49,24 @@ __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_bf16_kernel(
 
 }  // namespace
 
-hipError_t launch_bwd_pre_bf16(const Problem& p, const void* o, const void* dO, float* delta,
+template <class E>
+hipError_t launch_bwd_pre_e(const Problem& p, const void* o, const void* dO, float* delta,
                                hipStream_t s) {
   const long long n_rows = (long long)p.B * p.T * p.Hq;
   const dim3 grid((unsigned)((n_rows + PRE_ROWS - 1) / PRE_ROWS));
-  attn_bwd_pre_bf16_kernel<<<grid, PRE_THREADS, 0, s>>>(
+  attn_bwd_pre_kernel<E><<<grid, PRE_THREADS, 0, s>>>(
       static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), delta, p.T, p.Hq, n_rows);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre_bf16(const Problem& p, const void* o, const void* dO, float* delta,
+                               hipStream_t s) {
+  return launch_bwd_pre_e<Bf16>(p, o, dO, delta, s);
+}
+
+hipError_t launch_bwd_pre_f16(const Problem& p, const void* o, const void* dO, float* delta,
+                               hipStream_t s) {
+  return launch_bwd_pre_e<F16>(p, o, dO, delta, s);
 }
 
 }  // namespace rca

@@ -159,6 +159,55 @@ __device__ __forceinline__ u32x4_t lds_operand_T_swz(const uint16_t* tile, int r
   return o;
 }
 
+// Element types of the 16-bit kernels.  Each trait gives the matrix product,
+// the fp32 -> 16-bit pair conversion (round to nearest even: v_cvt_pk_bf16_f32,
+// v_cvt_pk_f16_f32), the 16-bit -> fp32 unpacking of the two halves of a dword
+// and the sum of a packed pair into an fp32 accumulator (v_dot2c against ones).
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+struct Bf16 {
+  static constexpr const char* name = "bf16";
+  __device__ static __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return mfma_32x32x16(a, b, c);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ static __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+  __device__ static __forceinline__ float add_pair(uint32_t w, float acc) { return add_bf16_pair(w, acc); }
+};
+
+struct F16 {
+  static constexpr const char* name = "f16";
+  __device__ static __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+    f16x2_t v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
+  __device__ static __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
+  __device__ static __forceinline__ float add_pair(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w),
+                                  __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc, false);
+  }
+};
+
+// Eight consecutive accumulator registers r0..r0+7 -> one 16-bit MFMA operand.
+template <class E>
+__device__ __forceinline__ u32x4_t pack_operand_e(const f32x16_t& acc, int r0) {
+  u32x4_t o;
+  o[0] = E::pack2(acc[r0 + 0], acc[r0 + 1]);
+  o[1] = E::pack2(acc[r0 + 2], acc[r0 + 3]);
+  o[2] = E::pack2(acc[r0 + 4], acc[r0 + 5]);
+  o[3] = E::pack2(acc[r0 + 6], acc[r0 + 7]);
+  return o;
+}
+
 __device__ __forceinline__ u32x4_t zero4u() {
   u32x4_t z;
   z[0] = z[1] = z[2] = z[3] = 0u;

@@ -53,6 +53,7 @@ static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
 
 // The work of unit `unit` (a pair of key blocks of one (batch, KV head), see
 // decode_unit) for a 512-thread workgroup; smem holds SMEM_BYTES.
+template <class E>
 __device__ __forceinline__ void unit_body(
     char* __restrict__ smem, int unit, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -177,8 +178,8 @@ __device__ __forceinline__ void unit_body(
       f32x16_t sacc = zero16();
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        sacc = mfma_32x32x16(lds_load16_swz(sQ, l32, 16 * c + 8 * g), kf[c], sacc);
-        pacc = mfma_32x32x16(lds_load16_swz(sdO, l32, 16 * c + 8 * g), vf[c], pacc);
+        sacc = E::mfma(lds_load16_swz(sQ, l32, 16 * c + 8 * g), kf[c], sacc);
+        pacc = E::mfma(lds_load16_swz(sdO, l32, 16 * c + 8 * g), vf[c], pacc);
       }
       // pacc now holds dP - delta.
       if ((causal && q0 == k0) || q0 + 31 >= T) {
@@ -200,14 +201,14 @@ __device__ __forceinline__ void unit_body(
           pacc[r] *= p;
         }
       }
-      const u32x4_t pb0 = pack_operand(sacc, 0), pb1 = pack_operand(sacc, 8);
-      const u32x4_t sb0 = pack_operand(pacc, 0), sb1 = pack_operand(pacc, 8);
+      const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
+      const u32x4_t sb0 = pack_operand_e<E>(pacc, 0), sb1 = pack_operand_e<E>(pacc, 8);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        dv_acc[db] = mfma_32x32x16(lds_operand_T_swz(sdO, 0, 32 * db, lane), pb0, dv_acc[db]);
-        dk_acc[db] = mfma_32x32x16(lds_operand_T_swz(sQ, 0, 32 * db, lane), sb0, dk_acc[db]);
-        dv_acc[db] = mfma_32x32x16(lds_operand_T_swz(sdO, 16, 32 * db, lane), pb1, dv_acc[db]);
-        dk_acc[db] = mfma_32x32x16(lds_operand_T_swz(sQ, 16, 32 * db, lane), sb1, dk_acc[db]);
+        dv_acc[db] = E::mfma(lds_operand_T_swz(sdO, 0, 32 * db, lane), pb0, dv_acc[db]);
+        dk_acc[db] = E::mfma(lds_operand_T_swz(sQ, 0, 32 * db, lane), sb0, dk_acc[db]);
+        dv_acc[db] = E::mfma(lds_operand_T_swz(sdO, 16, 32 * db, lane), pb1, dv_acc[db]);
+        dk_acc[db] = E::mfma(lds_operand_T_swz(sQ, 16, 32 * db, lane), sb1, dk_acc[db]);
       }
       wave_lds_fence();  // this buffer's reads complete before it is refilled
     }
@@ -248,10 +249,10 @@ __device__ __forceinline__ void unit_body(
       }
       const uint32_t out_off = (uint32_t)(k0 + kk) * kv_row + (uint32_t)kvh * kHeadDim * 2 + 8 * c4;
       u32x2_t ok, ov;
-      ok[0] = pack_bf16x2(sk.x * scale, sk.y * scale);
-      ok[1] = pack_bf16x2(sk.z * scale, sk.w * scale);
-      ov[0] = pack_bf16x2(sv.x, sv.y);
-      ov[1] = pack_bf16x2(sv.z, sv.w);
+      ok[0] = E::pack2(sk.x * scale, sk.y * scale);
+      ok[1] = E::pack2(sk.z * scale, sk.w * scale);
+      ov[0] = E::pack2(sv.x, sv.y);
+      ov[1] = E::pack2(sv.z, sv.w);
       bstore8(rdk, out_off, ok);  // rows past the sequence end are dropped
       bstore8(rdv, out_off, ov);
     }

@@ -42,6 +42,7 @@ constexpr int SMEM_BYTES = 4 * TILE_BYTES;  // [buffer][K, V]
 
 // The work of unit `unit` (one 128-row query tile of one (batch, query head),
 // see decode_unit) for a 512-thread workgroup; smem holds SMEM_BYTES.
+template <class E>
 __device__ __forceinline__ void unit_body(
     char* __restrict__ smem, int unit, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -134,8 +135,8 @@ __device__ __forceinline__ void unit_body(
       for (int s = 0; s < 4; ++s) {  // first product adds to a literal zero
         const u32x4_t ak = lds_load16_swz(sK, 32 * kh + l32, 16 * s + 8 * g);
         const u32x4_t av = lds_load16_swz(sV, 32 * kh + l32, 16 * s + 8 * g);
-        sacc = mfma_32x32x16(ak, qf[s], sacc);
-        pacc = mfma_32x32x16(av, df[s], pacc);
+        sacc = E::mfma(ak, qf[s], sacc);
+        pacc = E::mfma(av, df[s], pacc);
       }
       // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.
       if ((causal && kb0 + 31 > qw0) || kb0 + 32 > T) {
@@ -151,11 +152,11 @@ __device__ __forceinline__ void unit_body(
 #pragma unroll
         for (int r = 0; r < 16; ++r) pacc[r] *= fast_exp2(fmaf(sacc[r], scale_log2, -L2));
       }
-      const u32x4_t ds0 = pack_operand(pacc, 0), ds1 = pack_operand(pacc, 8);
+      const u32x4_t ds0 = pack_operand_e<E>(pacc, 0), ds1 = pack_operand_e<E>(pacc, 8);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        dq_acc[db] = mfma_32x32x16(lds_operand_T_swz(sK, 32 * kh, 32 * db, lane), ds0, dq_acc[db]);
-        dq_acc[db] = mfma_32x32x16(lds_operand_T_swz(sK, 32 * kh + 16, 32 * db, lane), ds1, dq_acc[db]);
+        dq_acc[db] = E::mfma(lds_operand_T_swz(sK, 32 * kh, 32 * db, lane), ds0, dq_acc[db]);
+        dq_acc[db] = E::mfma(lds_operand_T_swz(sK, 32 * kh + 16, 32 * db, lane), ds1, dq_acc[db]);
       }
     }
     wait_loads();  // the next tile has landed in LDS
@@ -183,8 +184,8 @@ __device__ __forceinline__ void unit_body(
       for (int j = 0; j < 4; ++j) {
         const float4 x = part[(4 * db + j) * 64];
         u32x2_t w;
-        w[0] = pack_bf16x2((dq_acc[db][4 * j + 0] + x.x) * scale, (dq_acc[db][4 * j + 1] + x.y) * scale);
-        w[1] = pack_bf16x2((dq_acc[db][4 * j + 2] + x.z) * scale, (dq_acc[db][4 * j + 3] + x.w) * scale);
+        w[0] = E::pack2((dq_acc[db][4 * j + 0] + x.x) * scale, (dq_acc[db][4 * j + 1] + x.y) * scale);
+        w[1] = E::pack2((dq_acc[db][4 * j + 2] + x.z) * scale, (dq_acc[db][4 * j + 3] + x.w) * scale);
         bstore8(rdq, qoff + 2 * (32 * db + 8 * j + 4 * g), w);
       }
     }

@@ -46,8 +46,8 @@ constexpr int PART_STRIDE = 36;  // floats per lane in the merge buffer (32 of O
 constexpr float kSlack = 8.0f;   // lazy-rescale threshold, base-2 units
 static_assert(4 * 64 * PART_STRIDE * 4 <= 4 * TILE * 2, "merge buffer must fit");
 
-template <bool kPosScale>
-__global__ __launch_bounds__(NTHREADS) void attn_fwd_bf16_kernel(
+template <bool kPosScale, class E>
+__global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv,
     float scale_log2, int causal) {
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_bf16_kernel(
       f32x16_t sacc = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        sacc = mfma_32x32x16(lds_load16(sK + (32 * kh + l32) * PITCH + 16 * s + 8 * g), qf[s], sacc);
+        sacc = E::mfma(lds_load16(sK + (32 * kh + l32) * PITCH + 16 * s + 8 * g), qf[s], sacc);
       // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.  The
       // tile maximum is taken over the raw scores (the scale is positive; for a
       // negative scale the minimum) and scaled once.
@@ -174,14 +174,14 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], scale_log2, -m_run));
       }
-      const u32x4_t pb0 = pack_operand(sacc, 0), pb1 = pack_operand(sacc, 8);
+      const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
       // Row sum of the bf16 probabilities that enter O (two per v_dot2c_f32_bf16).
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l_run = add_bf16_pair(pb1[i], add_bf16_pair(pb0[i], l_run));
+      for (int i = 0; i < 4; ++i) l_run = E::add_pair(pb1[i], E::add_pair(pb0[i], l_run));
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        oacc[db] = mfma_32x32x16(lds_operand_T(sV, PITCH, 32 * kh, 32 * db, lane), pb0, oacc[db]);
-        oacc[db] = mfma_32x32x16(lds_operand_T(sV, PITCH, 32 * kh + 16, 32 * db, lane), pb1, oacc[db]);
+        oacc[db] = E::mfma(lds_operand_T(sV, PITCH, 32 * kh, 32 * db, lane), pb0, oacc[db]);
+        oacc[db] = E::mfma(lds_operand_T(sV, PITCH, 32 * kh + 16, 32 * db, lane), pb1, oacc[db]);
       }
     }
     if (kt + 1 < n_kv) store_tile(cur ^ 1);
@@ -216,9 +216,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_bf16_kernel(
       for (int j = 0; j < 4; ++j) {
         const float4 x = *reinterpret_cast<const float4*>(slot + 16 * db + 4 * j);
         u32x2_t w;
-        w[0] = pack_bf16x2((oacc[db][4 * j + 0] * a0 + x.x * a1) * inv,
+        w[0] = E::pack2((oacc[db][4 * j + 0] * a0 + x.x * a1) * inv,
                            (oacc[db][4 * j + 1] * a0 + x.y * a1) * inv);
-        w[1] = pack_bf16x2((oacc[db][4 * j + 2] * a0 + x.z * a1) * inv,
+        w[1] = E::pack2((oacc[db][4 * j + 2] * a0 + x.z * a1) * inv,
                            (oacc[db][4 * j + 3] * a0 + x.w * a1) * inv);
         bstore8(ro, qoff + 2 * (32 * db + 8 * j + 4 * g), w);
       }
@@ -233,16 +233,27 @@ const char* fwd_bf16_tiles() {
   return "fwd_bf16{BM=128,BN=64,waves=8(4 query x 2 key),mfma=32x32x16}";
 }
 
-hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+template <class E>
+hipError_t launch_fwd_e(const Problem& p, const void* q, const void* k, const void* v, void* o,
                            float* lse, hipStream_t s) {
   const int n_qt = (p.T + BM - 1) / BM;
   const dim3 grid((unsigned)(n_qt * p.B * p.Hq));
-  auto kernel = p.scale_log2 >= 0.f ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>;
+  auto kernel = p.scale_log2 >= 0.f ? attn_fwd_kernel<true, E> : attn_fwd_kernel<false, E>;
   kernel<<<grid, NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, p.B, p.T, p.Hq, p.Hkv,
       p.scale_log2, p.causal);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                           float* lse, hipStream_t s) {
+  return launch_fwd_e<Bf16>(p, q, k, v, o, lse, s);
+}
+
+hipError_t launch_fwd_f16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                           float* lse, hipStream_t s) {
+  return launch_fwd_e<F16>(p, q, k, v, o, lse, s);
 }
 
 }  // namespace rca

@@ -18,16 +18,29 @@ struct Problem {
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
                            float* lse, hipStream_t s);
+hipError_t launch_fwd_f16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                           float* lse, hipStream_t s);
 hipError_t launch_bwd_pre_bf16(const Problem& p, const void* o, const void* dO, float* delta,
                                hipStream_t s);
+hipError_t launch_bwd_pre_f16(const Problem& p, const void* o, const void* dO, float* delta,
+                               hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                const void* dO, const float* lse, const float* delta, void* dk,
+                                void* dv, hipStream_t s);
+hipError_t launch_bwd_dkdv_f16(const Problem& p, const void* q, const void* k, const void* v,
                                 const void* dO, const float* lse, const float* delta, void* dk,
                                 void* dv, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
                               const void* dO, const float* lse, const float* delta, void* dq,
                               hipStream_t s);
+hipError_t launch_bwd_dq_f16(const Problem& p, const void* q, const void* k, const void* v,
+                              const void* dO, const float* lse, const float* delta, void* dq,
+                              hipStream_t s);
 // dK/dV and dQ in one grid; bitwise the two launches above.
 hipError_t launch_bwd_dkdv_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                   const void* dO, const float* lse, const float* delta, void* dq,
+                                   void* dk, void* dv, hipStream_t s);
+hipError_t launch_bwd_dkdv_dq_f16(const Problem& p, const void* q, const void* k, const void* v,
                                    const void* dO, const float* lse, const float* delta, void* dq,
                                    void* dk, void* dv, hipStream_t s);
 

@@ -21,13 +21,17 @@ at the pages' shapes:
   "Full-step profiling" (B=32, T=1024, 24 heads of 64);
 * ``tiny-f32``    -- a tiny fp32 multi-head case the oracle finishes at once;
 * ``gqa-8x4096-peaked`` -- a long-sequence stress case whose queries are
-  drawn with standard deviation 3 so that the softmax is peaked.
+  drawn with standard deviation 3 so that the softmax is peaked;
+* ``gqa-1x512-f16``, ``gqa-4x1024-f16`` -- the same shapes with float16 storage
+  (the adjacent input type: the same dense peak as bf16);
+* ``gqa-4x1024-noncausal`` -- the headline shape without the causal mask.
 
 Generation recipe: ``numpy.random.Generator(PCG64(seed))``; ``standard_normal``
 in float64 drawn in the order Q, K, V, dO, each in C order of its
 [B, T, H, D] shape; Q multiplied by ``q_std``; cast to float32; for bf16
-workloads rounded to bfloat16 with round-to-nearest-even.  The oracle sees the
-stored values widened exactly to float64.
+workloads rounded to bfloat16 with round-to-nearest-even (float16 workloads:
+numpy's float32 -> float16 conversion, also round-to-nearest-even).  The oracle
+sees the stored values widened exactly to float64.
 """
 from __future__ import annotations
 
@@ -44,7 +48,7 @@ class Workload:
     Hq: int
     Hkv: int
     D: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     seed: int
     q_std: float = 1.0
     scale: float = 0.125
@@ -92,6 +96,13 @@ WORKLOADS = {
     "gqa-8x4096-peaked": Workload("gqa-8x4096-peaked", 8, 4096, 12, 4, 64, "bf16", seed=5,
                                   q_std=3.0,
                                   description="bf16 causal GQA 12/4, 8 x 4096, Q ~ N(0, 9)"),
+    "gqa-1x512-f16": Workload("gqa-1x512-f16", 1, 512, 12, 4, 64, "f16", seed=6,
+                              description="fp16 causal GQA 12/4, 1 x 512"),
+    "gqa-4x1024-f16": Workload("gqa-4x1024-f16", 4, 1024, 12, 4, 64, "f16", seed=3,
+                               description="fp16 causal GQA 12/4, 4 x 1024"),
+    "gqa-4x1024-noncausal": Workload("gqa-4x1024-noncausal", 4, 1024, 12, 4, 64, "bf16", seed=3,
+                                     causal=False,
+                                     description="bf16 GQA 12/4, 4 x 1024, no causal mask"),
 }
 
 
@@ -124,8 +135,8 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
 class Inputs:
     """Stored inputs of one workload.
 
-    For ``bf16`` workloads the arrays are ``uint16`` bit patterns; for ``f32``
-    they are ``float32``.  Shapes: q, dO [B,T,Hq,D]; k, v [B,T,Hkv,D].
+    For ``bf16`` and ``f16`` workloads the arrays are ``uint16`` bit patterns;
+    for ``f32`` they are ``float32``.  Shapes: q, dO [B,T,Hq,D]; k, v [B,T,Hkv,D].
     """
     workload: Workload
     q: np.ndarray
@@ -137,6 +148,8 @@ class Inputs:
         a = getattr(self, name)
         if self.workload.dtype == "bf16":
             return bf16_bits_to_f32(a).astype(np.float64)
+        if self.workload.dtype == "f16":
+            return a.view(np.float16).astype(np.float64)
         return a.astype(np.float64)
 
 
@@ -151,5 +164,10 @@ def generate(w: Workload) -> Inputs:
         if name == "q" and w.q_std != 1.0:
             a *= w.q_std
         a = a.astype(np.float32)
-        out[name] = f32_to_bf16_bits(a) if w.dtype == "bf16" else a
+        if w.dtype == "bf16":
+            out[name] = f32_to_bf16_bits(a)
+        elif w.dtype == "f16":
+            out[name] = a.astype(np.float16).view(np.uint16)
+        else:
+            out[name] = a
     return Inputs(w, **out)

@@ -15,7 +15,8 @@ from reproducible_causal_attention_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["tiny-f32", "gqa-1x512", "gqa-4x1024"])
+@pytest.mark.parametrize("name", ["tiny-f32", "gqa-1x512", "gqa-4x1024", "gqa-1x512-f16",
+                                  "gqa-4x1024-f16", "gqa-4x1024-noncausal"])
 def test_workload_full_parity(name):
     w = W.WORKLOADS[name]
     inp = W.generate(w)
@@ -51,6 +52,10 @@ EDGE_CASES = [
     (1, 100, 4, 2, "f32", True, 1.0),
     (2, 65, 3, 1, "f32", False, 1.0),
     (1, 300, 2, 2, "f32", True, 3.0),
+    (1, 1, 2, 1, "f16", True, 1.0),
+    (2, 1000, 6, 3, "f16", True, 1.0),
+    (1, 333, 12, 1, "f16", True, 3.0),    # peaked softmax in fp16
+    (2, 77, 6, 2, "f16", False, 1.0),
 ]
 
 
