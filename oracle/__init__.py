@@ -10,6 +10,7 @@ arithmetic.
 ``attention``  vectorised numpy fp64 implementation (materialises the score
                matrix one (batch, head) at a time).
 ``brute``      pure-Python scalar loops with ``math.fsum``, for tiny inputs.
+``rope``       rotary position embedding of q and k ahead of the attention.
 """
 from .attention import (  # noqa: F401
     kv_head_of,
@@ -20,3 +21,4 @@ from .attention import (  # noqa: F401
     ref_bwd_group,
 )
 from .brute import brute_fwd, brute_bwd  # noqa: F401
+from .rope import apply_rope, apply_rope_transpose, ref_fwd_rope, ref_bwd_rope  # noqa: F401

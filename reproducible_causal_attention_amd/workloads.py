@@ -111,6 +111,15 @@ def custom(B, T, Hq, Hkv, D=64, dtype="bf16", seed=0, q_std=1.0, scale=0.125,
     return Workload(name, B, T, Hq, Hkv, D, dtype, seed, q_std, scale, causal)
 
 
+def rope_tables(T: int, D: int, base: float = 10000.0):
+    """Caller-side rotary tables: cos and sin of t * base^(-2i/D) for positions
+    t < T and pairs i < D/2, computed in float64 and stored as float32 [T, D/2]
+    (the form the kernels and the oracle both take as an input)."""
+    i = np.arange(D // 2, dtype=np.float64)
+    ang = np.arange(T, dtype=np.float64)[:, None] * np.power(base, -2.0 * i / D)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 # --------------------------------------------------------------------------
 # bfloat16 storage helpers (storage format only, not attention arithmetic)
 # --------------------------------------------------------------------------
