@@ -47,8 +47,10 @@
  * failed validation enqueues nothing.  ATTN_ERR_INVALID_ARG: a null pointer; a
  * size <= 0; Hq not a multiple of Hkv; causal not 0 or 1; scale not finite; a
  * pointer not 16-byte aligned; an output range overlapping an input range or
- * another output; a workspace smaller than attn_bwd_workspace_bytes(); sizes
- * beyond the limits below.  ATTN_ERR_UNSUPPORTED: D != 64 or an unknown dtype.
+ * another output; a workspace smaller than attn_bwd_workspace_bytes() (or
+ * attn_bwd_rope_workspace_bytes() for attn_bwd_rope); sizes
+ * beyond the limits below.  ATTN_ERR_UNSUPPORTED: D != 64, an unknown dtype, or
+ * ATTN_F32 in a rotary entry point.
  * ATTN_ERR_HIP: the HIP runtime reported an error for a launch (the value of
  * hipGetLastError() after the launch; an error pending from an earlier,
  * unrelated runtime call is discarded before the launch, so it is not reported
@@ -142,6 +144,45 @@ attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const void* v, cons
                                const float* lse, const float* delta, void* dq, void* dk, void* dv,
                                int B, int T, int Hq, int Hkv, int D, float scale, int causal,
                                attn_dtype_t dtype, void* stream);
+
+/* Rotary position embedding fused into the attention (ATTN_BF16 and ATTN_F16
+ * only; ATTN_F32 gives ATTN_ERR_UNSUPPORTED).  "Training a 100M transformer in
+ * pure Rust: RustingBrain vs PyTorch and TensorFlow", section "The setup", puts
+ * rotary positions in the model without fixing a convention; the one taken is
+ * the original adjacent-pair rotation: at position t, pair i = (x[2i], x[2i+1])
+ * of every query and key vector becomes
+ *   (x[2i] c - x[2i+1] s,  x[2i] s + x[2i+1] c),  c = rope_cos[t][i], s = rope_sin[t][i],
+ * the same positions 0 .. T-1 for queries and keys; v is not rotated.
+ * rope_cos and rope_sin are [T, D/2] float32 tables that the caller fills (any
+ * base or scaling); they are inputs like q.  The rotated pair is rounded to the
+ * input dtype before the products, as an unfused rotation that stores its
+ * result would round it.
+ *
+ * attn_fwd_rope: attn_fwd on the rotated q', k'.  o and lse as there. */
+attn_status_t attn_fwd_rope(const void* q, const void* k, const void* v, const float* rope_cos,
+                            const float* rope_sin, void* o, float* lse, int B, int T, int Hq,
+                            int Hkv, int D, float scale, int causal, attn_dtype_t dtype,
+                            void* stream);
+
+/* Bytes of device workspace attn_bwd_rope needs: delta (B*Hq*T float32), then
+ * the rotated q' ([B, T, Hq, D]) and k' ([B, T, Hkv, D]) in the input dtype,
+ * each rounded up to 256 bytes.  Returns 0 for invalid sizes or ATTN_F32. */
+size_t attn_bwd_rope_workspace_bytes(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype);
+
+/* Backward of attn_fwd_rope: dq, dk, dv with respect to the unrotated q, k and
+ * v.  o and lse must be the outputs of attn_fwd_rope for the same inputs and
+ * tables.  Enqueues a preparation kernel (delta, q' and k' into the workspace,
+ * rotated with the same arithmetic as the forward, so the same bits) and the
+ * co-launched dK/dV + dQ grid on q', k', whose epilogues map dq and dk back
+ * through the transpose of each pair's rotation:
+ *   (g[2i] c + g[2i+1] s,  -g[2i] s + g[2i+1] c).
+ * Ownership, overlap and workspace rules as attn_bwd; the workspace must hold
+ * attn_bwd_rope_workspace_bytes() bytes and is clobbered. */
+attn_status_t attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dO, const float* rope_cos,
+                            const float* rope_sin, void* dq, void* dk, void* dv, int B, int T,
+                            int Hq, int Hkv, int D, float scale, int causal, attn_dtype_t dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status_t status);

@@ -7,6 +7,7 @@ raise; there is no fallback.
 
 Layouts: q, o, dO, dq are [B, T, Hq, 64]; k, v, dk, dv are [B, T, Hkv, 64]
 (contiguous, bfloat16, float16 or float32); lse and delta are [B, Hq, T] float32.
+The rotary variants take cos and sin tables [T, 32] float32 (bf16 / fp16 only).
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 
 EXPORTED = (
     "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-    "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dkdv_dq", "attn_status_string", "attn_build_info",
+    "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dkdv_dq", "attn_fwd_rope",
+    "attn_bwd_rope_workspace_bytes", "attn_bwd_rope", "attn_status_string", "attn_build_info",
 )
 
 _lib = None
@@ -60,8 +62,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, P, *sizes, F, I, I, P]
     lib.attn_bwd_dq.argtypes = [P, P, P, P, P, P, P, *sizes, F, I, I, P]
     lib.attn_bwd_dkdv_dq.argtypes = [P, P, P, P, P, P, P, P, P, *sizes, F, I, I, P]
+    lib.attn_fwd_rope.argtypes = [P, P, P, P, P, P, P, *sizes, F, I, I, P]
+    lib.attn_bwd_rope_workspace_bytes.argtypes = [*sizes, I]
+    lib.attn_bwd_rope_workspace_bytes.restype = Z
+    lib.attn_bwd_rope.argtypes = [P, P, P, P, P, P, P, P, P, P, P, *sizes, F, I, I, P, Z, P]
     for name in ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
-                 "attn_bwd_dkdv_dq"):
+                 "attn_bwd_dkdv_dq", "attn_fwd_rope", "attn_bwd_rope"):
         getattr(lib, name).restype = I
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -189,4 +195,46 @@ def bwd_dkdv_dq(q, k, v, dO, lse, delta, scale=None, causal=True):
     _check(lib.attn_bwd_dkdv_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
                                 _ptr(dq), _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale,
                                 int(bool(causal)), _dtype_code(q), _stream()))
+    return dq, dk, dv
+
+
+def _tables(cos, sin, T, D):
+    for t in (cos, sin):
+        if t.dtype != torch.float32 or tuple(t.shape) != (T, D // 2):
+            raise ValueError(f"rotary tables must be float32 [T, D/2] = [{T}, {D // 2}]")
+    return _ptr(cos), _ptr(sin)
+
+
+def fwd_rope(q, k, v, cos, sin, scale=None, causal=True):
+    """Forward with rotary embedding of q and k (adjacent pairs, tables [T, D/2]):
+    returns ``(o, lse)``."""
+    lib = load_library()
+    B, T, Hq, Hkv, D = _shapes(q, k)
+    scale = default_scale(D) if scale is None else float(scale)
+    pc, ps = _tables(cos, sin, T, D)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), pc, ps, _ptr(o), _ptr(lse), B, T, Hq,
+                             Hkv, D, scale, int(bool(causal)), _dtype_code(q), _stream()))
+    return o, lse
+
+
+def rope_workspace_bytes(B, T, Hq, Hkv, D, dtype_code) -> int:
+    return int(load_library().attn_bwd_rope_workspace_bytes(B, T, Hq, Hkv, D, dtype_code))
+
+
+def bwd_rope(q, k, v, o, lse, dO, cos, sin, scale=None, causal=True, workspace=None):
+    """Backward of ``fwd_rope``: ``(dq, dk, dv)`` with respect to the unrotated q, k, v."""
+    lib = load_library()
+    B, T, Hq, Hkv, D = _shapes(q, k)
+    scale = default_scale(D) if scale is None else float(scale)
+    pc, ps = _tables(cos, sin, T, D)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = rope_workspace_bytes(B, T, Hq, Hkv, D, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), pc, ps,
+                             _ptr(dq), _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale,
+                             int(bool(causal)), _dtype_code(q), _ptr(workspace), workspace.numel(),
+                             _stream()))
     return dq, dk, dv

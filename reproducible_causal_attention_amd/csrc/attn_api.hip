@@ -96,6 +96,13 @@ attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E
 // the status after the launch is the launch's own.
 void discard_stale_error() { (void)hipGetLastError(); }
 
+// The rotary variants run in the 16-bit types only.
+attn_status_t check_rope_dtype(attn_dtype_t dtype) {
+  return dtype == ATTN_BF16 || dtype == ATTN_F16 ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
 #define ATTN_TRY(expr)                       \
   do {                                       \
     const attn_status_t st_ = (expr);        \
@@ -125,8 +132,7 @@ ATTN_EXPORT attn_status_t attn_fwd(const void* q, const void* k, const void* v, 
 
 ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype) {
   if (check_shape(B, T, Hq, Hkv, D, dtype) != ATTN_OK) return 0;
-  const size_t bytes = (size_t)B * Hq * T * sizeof(float);
-  return (bytes + 255) / 256 * 256;
+  return round256((size_t)B * Hq * T * sizeof(float));
 }
 
 ATTN_EXPORT attn_status_t attn_bwd_preprocess(const void* o, const void* dO, float* delta, int B,
@@ -244,6 +250,73 @@ ATTN_EXPORT attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const v
     return from_hip(rca::launch_bwd_dkdv_dq_f16(p, q, k, v, dO, lse, delta, dq, dk, dv, s));
   ATTN_TRY(from_hip(rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s)));
   return from_hip(rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
+}
+
+ATTN_EXPORT attn_status_t attn_fwd_rope(const void* q, const void* k, const void* v,
+                                        const float* rope_cos, const float* rope_sin, void* o,
+                                        float* lse, int B, int T, int Hq, int Hkv, int D,
+                                        float scale, int causal, attn_dtype_t dtype, void* stream) {
+  ATTN_TRY(check_ptrs({q, k, v, rope_cos, rope_sin, o, lse}));
+  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_scalars(scale, causal));
+  ATTN_TRY(check_rope_dtype(dtype));
+  const size_t qb = (size_t)B * T * Hq * D * 2, kb = (size_t)B * T * Hkv * D * 2;
+  const size_t lb = (size_t)B * Hq * T * sizeof(float), tb = (size_t)T * (D / 2) * sizeof(float);
+  ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(rope_cos, tb),
+                           span_of(rope_sin, tb)},
+                          {span_of(o, qb), span_of(lse, lb)}));
+  discard_stale_error();
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(dtype == ATTN_BF16
+                      ? rca::launch_fwd_rope_bf16(p, q, k, v, rope_cos, rope_sin, o, lse, s)
+                      : rca::launch_fwd_rope_f16(p, q, k, v, rope_cos, rope_sin, o, lse, s));
+}
+
+ATTN_EXPORT size_t attn_bwd_rope_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
+                                                 attn_dtype_t dtype) {
+  if (check_shape(B, T, Hq, Hkv, D, dtype) != ATTN_OK || check_rope_dtype(dtype) != ATTN_OK)
+    return 0;
+  return round256((size_t)B * Hq * T * sizeof(float)) + round256((size_t)B * T * Hq * D * 2) +
+         round256((size_t)B * T * Hkv * D * 2);
+}
+
+ATTN_EXPORT attn_status_t attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
+                                        const float* lse, const void* dO, const float* rope_cos,
+                                        const float* rope_sin, void* dq, void* dk, void* dv, int B,
+                                        int T, int Hq, int Hkv, int D, float scale, int causal,
+                                        attn_dtype_t dtype, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  ATTN_TRY(check_ptrs({q, k, v, o, lse, dO, rope_cos, rope_sin, dq, dk, dv, workspace}));
+  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_scalars(scale, causal));
+  ATTN_TRY(check_rope_dtype(dtype));
+  const size_t need = attn_bwd_rope_workspace_bytes(B, T, Hq, Hkv, D, dtype);
+  if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
+  const size_t qb = (size_t)B * T * Hq * D * 2, kb = (size_t)B * T * Hkv * D * 2;
+  const size_t lb = (size_t)B * Hq * T * sizeof(float), tb = (size_t)T * (D / 2) * sizeof(float);
+  ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(o, qb),
+                           span_of(lse, lb), span_of(dO, qb), span_of(rope_cos, tb),
+                           span_of(rope_sin, tb)},
+                          {span_of(dq, qb), span_of(dk, kb), span_of(dv, kb),
+                           span_of(workspace, need)}));
+  char* ws = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws);
+  void* q_rot = ws + round256(lb);
+  void* k_rot = ws + round256(lb) + round256(qb);
+  discard_stale_error();
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16) {
+    ATTN_TRY(from_hip(rca::launch_bwd_rope_prep_bf16(p, o, dO, q, k, rope_cos, rope_sin, delta,
+                                                     q_rot, k_rot, s)));
+    return from_hip(rca::launch_bwd_dkdv_dq_rope_bf16(p, q_rot, k_rot, v, dO, lse, delta, rope_cos,
+                                                      rope_sin, dq, dk, dv, s));
+  }
+  ATTN_TRY(from_hip(rca::launch_bwd_rope_prep_f16(p, o, dO, q, k, rope_cos, rope_sin, delta, q_rot,
+                                                  k_rot, s)));
+  return from_hip(rca::launch_bwd_dkdv_dq_rope_f16(p, q_rot, k_rot, v, dO, lse, delta, rope_cos,
+                                                   rope_sin, dq, dk, dv, s));
 }
 
 ATTN_EXPORT const char* attn_status_string(attn_status_t status) {

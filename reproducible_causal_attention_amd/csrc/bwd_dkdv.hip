@@ -12,8 +12,8 @@ __global__ __launch_bounds__(dkdv::NTHREADS) void attn_bwd_dkdv_kernel(
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
     float scale, float scale_log2, int causal) {
   __shared__ __attribute__((aligned(16))) char smem[dkdv::SMEM_BYTES];
-  dkdv::unit_body<E>(smem, blockIdx.x, q, k, v, dO, lse, delta, dk, dv, B, T, Hq, Hkv, scale,
-                  scale_log2, causal);
+  dkdv::unit_body<E, false>(smem, blockIdx.x, q, k, v, dO, lse, delta, nullptr, nullptr, dk, dv, B,
+                            T, Hq, Hkv, scale, scale_log2, causal);
 }
 
 }  // namespace

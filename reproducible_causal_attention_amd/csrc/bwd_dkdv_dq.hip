@@ -20,37 +20,41 @@ constexpr int kSmemBytes = dkdv::SMEM_BYTES > dqb::SMEM_BYTES ? dkdv::SMEM_BYTES
 
 // Workgroup i < n_dq runs dQ unit i; n_dq <= i < kv_base exit at once (padding,
 // so that dK/dV unit u keeps the XCD, i % 8, it has in its own grid); then dK/dV
-// unit i - kv_base.
-template <class E>
+// unit i - kv_base.  kRope: q and k are the rotated q', k' and dq, dk are mapped
+// back through the rotations in the epilogues (tables rcos, rsin).
+template <class E, bool kRope>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T,
-    int Hq, int Hkv, float scale, float scale_log2, int causal, int n_dq, int kv_base) {
+    const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
+    float scale, float scale_log2, int causal, int n_dq, int kv_base) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int i = blockIdx.x;
   if (i < n_dq) {
-    dqb::unit_body<E>(smem, i, q, k, v, dO, lse, delta, dq, B, T, Hq, Hkv, scale, scale_log2, causal);
+    dqb::unit_body<E, kRope>(smem, i, q, k, v, dO, lse, delta, rcos, rsin, dq, B, T, Hq, Hkv,
+                             scale, scale_log2, causal);
   } else if (i >= kv_base) {
-    dkdv::unit_body<E>(smem, i - kv_base, q, k, v, dO, lse, delta, dk, dv, B, T, Hq, Hkv, scale,
-                    scale_log2, causal);
+    dkdv::unit_body<E, kRope>(smem, i - kv_base, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T,
+                              Hq, Hkv, scale, scale_log2, causal);
   }
 }
 
 }  // namespace
 
-template <class E>
+template <class E, bool kRope>
 hipError_t launch_bwd_dkdv_dq_e(const Problem& p, const void* q, const void* k, const void* v,
-                                   const void* dO, const float* lse, const float* delta, void* dq,
-                                   void* dk, void* dv, hipStream_t s) {
+                                const void* dO, const float* lse, const float* delta,
+                                const float* rcos, const float* rsin, void* dq, void* dk, void* dv,
+                                hipStream_t s) {
   const int n_dq = ((p.T + dqb::BM - 1) / dqb::BM) * p.B * p.Hq;
   const int kv_base = (n_dq + 7) / 8 * 8;
   const int nkb = (p.T + 31) / 32;
   const int n_kv = (nkb + 1) / 2 * p.B * p.Hkv;
   const dim3 grid((unsigned)(kv_base + n_kv));
-  attn_bwd_dkdv_dq_kernel<E><<<grid, kThreads, 0, s>>>(
+  attn_bwd_dkdv_dq_kernel<E, kRope><<<grid, kThreads, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta,
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta, rcos, rsin,
       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), p.B,
       p.T, p.Hq, p.Hkv, p.scale, p.scale_log2, p.causal, n_dq, kv_base);
   return hipGetLastError();
@@ -59,13 +63,27 @@ hipError_t launch_bwd_dkdv_dq_e(const Problem& p, const void* q, const void* k, 
 hipError_t launch_bwd_dkdv_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
                                    const void* dO, const float* lse, const float* delta, void* dq,
                                    void* dk, void* dv, hipStream_t s) {
-  return launch_bwd_dkdv_dq_e<Bf16>(p, q, k, v, dO, lse, delta, dq, dk, dv, s);
+  return launch_bwd_dkdv_dq_e<Bf16, false>(p, q, k, v, dO, lse, delta, nullptr, nullptr, dq, dk, dv, s);
 }
 
 hipError_t launch_bwd_dkdv_dq_f16(const Problem& p, const void* q, const void* k, const void* v,
-                                   const void* dO, const float* lse, const float* delta, void* dq,
-                                   void* dk, void* dv, hipStream_t s) {
-  return launch_bwd_dkdv_dq_e<F16>(p, q, k, v, dO, lse, delta, dq, dk, dv, s);
+                                  const void* dO, const float* lse, const float* delta, void* dq,
+                                  void* dk, void* dv, hipStream_t s) {
+  return launch_bwd_dkdv_dq_e<F16, false>(p, q, k, v, dO, lse, delta, nullptr, nullptr, dq, dk, dv, s);
+}
+
+hipError_t launch_bwd_dkdv_dq_rope_bf16(const Problem& p, const void* q_rot, const void* k_rot,
+                                        const void* v, const void* dO, const float* lse,
+                                        const float* delta, const float* rcos, const float* rsin,
+                                        void* dq, void* dk, void* dv, hipStream_t s) {
+  return launch_bwd_dkdv_dq_e<Bf16, true>(p, q_rot, k_rot, v, dO, lse, delta, rcos, rsin, dq, dk, dv, s);
+}
+
+hipError_t launch_bwd_dkdv_dq_rope_f16(const Problem& p, const void* q_rot, const void* k_rot,
+                                       const void* v, const void* dO, const float* lse,
+                                       const float* delta, const float* rcos, const float* rsin,
+                                       void* dq, void* dk, void* dv, hipStream_t s) {
+  return launch_bwd_dkdv_dq_e<F16, true>(p, q_rot, k_rot, v, dO, lse, delta, rcos, rsin, dq, dk, dv, s);
 }
 
 }  // namespace rca

@@ -18,10 +18,11 @@ constexpr int PRE_THREADS = 256;
 constexpr int PRE_ROWS = PRE_THREADS / 8;  // 8 lanes x 8 elements per 64-wide row
 
 template <class E>
-__global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_kernel(
-    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO, float* __restrict__ delta,
-    int T, int Hq, long long n_rows) {
-  const long long row = (long long)blockIdx.x * PRE_ROWS + (threadIdx.x >> 3);
+__device__ __forceinline__ void delta_rows(int blk, const uint16_t* __restrict__ o,
+                                           const uint16_t* __restrict__ dO,
+                                           float* __restrict__ delta, int T, int Hq,
+                                           long long n_rows) {
+  const long long row = (long long)blk * PRE_ROWS + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
   float acc = 0.f;
   if (row < n_rows) {
@@ -47,6 +48,56 @@ __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_kernel(
   }
 }
 
+template <class E>
+__global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_kernel(
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO, float* __restrict__ delta,
+    int T, int Hq, long long n_rows) {
+  delta_rows<E>(blockIdx.x, o, dO, delta, T, Hq, n_rows);
+}
+
+// Backward preparation with rotary embedding: blocks [0, nb) write delta exactly
+// as attn_bwd_pre_kernel does, blocks [nb, 2nb) the rotated q rows and the rest
+// the rotated k rows (rope_rotate, as the forward rotates them as it loads:
+// the same bits), which the dK/dV and dQ kernels then read in place of q, k.
+template <class E>
+__global__ __launch_bounds__(PRE_THREADS) void attn_bwd_rope_prep_kernel(
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, float* __restrict__ delta,
+    uint16_t* __restrict__ q_rot, uint16_t* __restrict__ k_rot, int T, int Hq, int Hkv,
+    long long n_qrows, long long n_krows, int nb) {
+  int blk = blockIdx.x;
+  if (blk < nb) {
+    delta_rows<E>(blk, o, dO, delta, T, Hq, n_qrows);
+    return;
+  }
+  blk -= nb;
+  const uint16_t* src = q;
+  uint16_t* dst = q_rot;
+  int H = Hq;
+  long long n_rows = n_qrows;
+  if (blk >= nb) {
+    blk -= nb;
+    src = k;
+    dst = k_rot;
+    H = Hkv;
+    n_rows = n_krows;
+  }
+  const long long row = (long long)blk * PRE_ROWS + (threadIdx.x >> 3);  // [b][t][h]
+  const int part = threadIdx.x & 7;  // elements 8*part .. +7, pairs 4*part .. +3
+  if (row < n_rows) {
+    const int t = (int)((row / H) % T);
+    u32x4_t x = gload16(src + row * kHeadDim + part * 8);
+    const float4 c = *reinterpret_cast<const float4*>(rcos + (size_t)t * 32 + part * 4);
+    const float4 s = *reinterpret_cast<const float4*>(rsin + (size_t)t * 32 + part * 4);
+    x[0] = rope_rotate<E>(x[0], c.x, s.x);
+    x[1] = rope_rotate<E>(x[1], c.y, s.y);
+    x[2] = rope_rotate<E>(x[2], c.z, s.z);
+    x[3] = rope_rotate<E>(x[3], c.w, s.w);
+    *reinterpret_cast<u32x4_t*>(dst + row * kHeadDim + part * 8) = x;
+  }
+}
+
 }  // namespace
 
 template <class E>
@@ -57,6 +108,33 @@ hipError_t launch_bwd_pre_e(const Problem& p, const void* o, const void* dO, flo
   attn_bwd_pre_kernel<E><<<grid, PRE_THREADS, 0, s>>>(
       static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), delta, p.T, p.Hq, n_rows);
   return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_bwd_rope_prep_e(const Problem& p, const void* o, const void* dO, const void* q,
+                                  const void* k, const float* rcos, const float* rsin,
+                                  float* delta, void* q_rot, void* k_rot, hipStream_t s) {
+  const long long n_q = (long long)p.B * p.T * p.Hq, n_k = (long long)p.B * p.T * p.Hkv;
+  const int nb = (int)((n_q + PRE_ROWS - 1) / PRE_ROWS);
+  const int nbk = (int)((n_k + PRE_ROWS - 1) / PRE_ROWS);
+  const dim3 grid((unsigned)(2 * nb + nbk));
+  attn_bwd_rope_prep_kernel<E><<<grid, PRE_THREADS, 0, s>>>(
+      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO),
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rcos, rsin, delta,
+      static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), p.T, p.Hq, p.Hkv, n_q, n_k, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_rope_prep_bf16(const Problem& p, const void* o, const void* dO, const void* q,
+                                     const void* k, const float* rcos, const float* rsin,
+                                     float* delta, void* q_rot, void* k_rot, hipStream_t s) {
+  return launch_bwd_rope_prep_e<Bf16>(p, o, dO, q, k, rcos, rsin, delta, q_rot, k_rot, s);
+}
+
+hipError_t launch_bwd_rope_prep_f16(const Problem& p, const void* o, const void* dO, const void* q,
+                                    const void* k, const float* rcos, const float* rsin,
+                                    float* delta, void* q_rot, void* k_rot, hipStream_t s) {
+  return launch_bwd_rope_prep_e<F16>(p, o, dO, q, k, rcos, rsin, delta, q_rot, k_rot, s);
 }
 
 hipError_t launch_bwd_pre_bf16(const Problem& p, const void* o, const void* dO, float* delta,

@@ -208,6 +208,25 @@ __device__ __forceinline__ u32x4_t pack_operand_e(const f32x16_t& acc, int r0) {
   return o;
 }
 
+// The float whose bits are w.  Takes w by value: __builtin_bit_cast applied
+// directly to a vector element (v[e]) reads element 0 with this compiler.
+__device__ __forceinline__ float bits_to_float(uint32_t w) { return __builtin_bit_cast(float, w); }
+
+// Rotary embedding of one packed pair (x[2i], x[2i+1]) by (c, s) = (cos, sin) of
+// its angle: (x0 c - x1 s, x0 s + x1 c), each an explicit fma so every kernel
+// that rotates the same pair gets the same bits.
+template <class E>
+__device__ __forceinline__ uint32_t rope_rotate(uint32_t w, float c, float s) {
+  const float x0 = E::lo(w), x1 = E::hi(w);
+  return E::pack2(fmaf(x0, c, -(x1 * s)), fmaf(x0, s, x1 * c));
+}
+// The transpose, applied to an fp32 gradient pair (g0, g1): (g0 c + g1 s, -g0 s + g1 c).
+__device__ __forceinline__ void rope_rotate_back(float& g0, float& g1, float c, float s) {
+  const float a = fmaf(g0, c, g1 * s), b = fmaf(g1, c, -(g0 * s));
+  g0 = a;
+  g1 = b;
+}
+
 __device__ __forceinline__ u32x4_t zero4u() {
   u32x4_t z;
   z[0] = z[1] = z[2] = z[3] = 0u;

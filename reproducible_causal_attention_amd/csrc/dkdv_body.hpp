@@ -53,13 +53,17 @@ static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
 
 // The work of unit `unit` (a pair of key blocks of one (batch, KV head), see
 // decode_unit) for a 512-thread workgroup; smem holds SMEM_BYTES.
-template <class E>
+// kRope: q and k are the rotated q', k' (rotary embedding); the epilogue maps
+// dK back through each pair's rotation transpose with the tables rcos, rsin
+// ([T, 32] float32), so dk is the gradient with respect to the unrotated k.
+template <class E, bool kRope>
 __device__ __forceinline__ void unit_body(
-    char* __restrict__ smem, int unit, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    char* __restrict__ smem, int unit, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
-    float scale, float scale_log2, int causal) {
-
+    const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
+    int causal) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
@@ -249,8 +253,15 @@ __device__ __forceinline__ void unit_body(
       }
       const uint32_t out_off = (uint32_t)(k0 + kk) * kv_row + (uint32_t)kvh * kHeadDim * 2 + 8 * c4;
       u32x2_t ok, ov;
-      ok[0] = E::pack2(sk.x * scale, sk.y * scale);
-      ok[1] = E::pack2(sk.z * scale, sk.w * scale);
+      float g0 = sk.x * scale, g1 = sk.y * scale, g2 = sk.z * scale, g3 = sk.w * scale;
+      if (kRope) {  // d = 4*c4 .. +3: pairs 2*c4, 2*c4 + 1 of key k0 + kk
+        const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * 128u), rts = make_rsrc(rsin, (uint32_t)T * 128u);
+        const uint32_t toff = ((uint32_t)(k0 + kk) * 32 + 2 * c4) * 4;
+        rope_rotate_back(g0, g1, bload_f32(rtc, toff), bload_f32(rts, toff));
+        rope_rotate_back(g2, g3, bload_f32(rtc, toff + 4), bload_f32(rts, toff + 4));
+      }
+      ok[0] = E::pack2(g0, g1);
+      ok[1] = E::pack2(g2, g3);
       ov[0] = E::pack2(sv.x, sv.y);
       ov[1] = E::pack2(sv.z, sv.w);
       bstore8(rdk, out_off, ok);  // rows past the sequence end are dropped

@@ -42,13 +42,16 @@ constexpr int SMEM_BYTES = 4 * TILE_BYTES;  // [buffer][K, V]
 
 // The work of unit `unit` (one 128-row query tile of one (batch, query head),
 // see decode_unit) for a 512-thread workgroup; smem holds SMEM_BYTES.
-template <class E>
+// kRope: q and k are the rotated q', k' (rotary embedding); the epilogue maps
+// dQ back through each pair's rotation transpose with the tables rcos, rsin
+// ([T, 32] float32), so dq is the gradient with respect to the unrotated q.
+template <class E, bool kRope>
 __device__ __forceinline__ void unit_body(
-    char* __restrict__ smem, int unit, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    char* __restrict__ smem, int unit, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ dq, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
-    int causal) {
-
+    const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dq,
+    int B, int T, int Hq, int Hkv, float scale, float scale_log2, int causal) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
@@ -184,8 +187,16 @@ __device__ __forceinline__ void unit_body(
       for (int j = 0; j < 4; ++j) {
         const float4 x = part[(4 * db + j) * 64];
         u32x2_t w;
-        w[0] = E::pack2((dq_acc[db][4 * j + 0] + x.x) * scale, (dq_acc[db][4 * j + 1] + x.y) * scale);
-        w[1] = E::pack2((dq_acc[db][4 * j + 2] + x.z) * scale, (dq_acc[db][4 * j + 3] + x.w) * scale);
+        float g0 = (dq_acc[db][4 * j + 0] + x.x) * scale, g1 = (dq_acc[db][4 * j + 1] + x.y) * scale;
+        float g2 = (dq_acc[db][4 * j + 2] + x.z) * scale, g3 = (dq_acc[db][4 * j + 3] + x.w) * scale;
+        if (kRope) {  // d = 32db + 8j + 4g + 0..3: pairs 16db + 4j + 2g + 0, 1 of row my_q
+          const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * 128u), rts = make_rsrc(rsin, (uint32_t)T * 128u);
+          const uint32_t toff = ((uint32_t)my_q * 32 + 16 * db + 4 * j + 2 * g) * 4;
+          rope_rotate_back(g0, g1, bload_f32(rtc, toff), bload_f32(rts, toff));
+          rope_rotate_back(g2, g3, bload_f32(rtc, toff + 4), bload_f32(rts, toff + 4));
+        }
+        w[0] = E::pack2(g0, g1);
+        w[1] = E::pack2(g2, g3);
         bstore8(rdq, qoff + 2 * (32 * db + 8 * j + 4 * g), w);
       }
     }

@@ -46,11 +46,13 @@ constexpr int PART_STRIDE = 36;  // floats per lane in the merge buffer (32 of O
 constexpr float kSlack = 8.0f;   // lazy-rescale threshold, base-2 units
 static_assert(4 * 64 * PART_STRIDE * 4 <= 4 * TILE * 2, "merge buffer must fit");
 
-template <bool kPosScale, class E>
+// kRope: q and k are rotated as they are loaded (rotary tables rcos, rsin:
+// [T, 32] float32, pair i of position t at t*32 + i), v is not.
+template <bool kPosScale, class E, bool kRope>
 __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv,
-    float scale_log2, int causal) {
+    const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ o,
+    float* __restrict__ lse, int B, int T, int Hq, int Hkv, float scale_log2, int causal) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
@@ -89,7 +91,26 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
   u32x4_t qf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s] = bload16(rq, qoff + 32 * s + 16 * g);
+  // Rotary tables (rows past the sequence end read as zero, like their q and k rows).
+  const rsrc_t rtc = make_rsrc(rcos, kRope ? (uint32_t)T * 128u : 0u);
+  const rsrc_t rts = make_rsrc(rsin, kRope ? (uint32_t)T * 128u : 0u);
+  u32x4_t qc[4], qsn[4];
+  if (kRope) {  // lane's pairs of chunk s: i = 8s + 4g + 0..3 of row my_q
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qc[s] = bload16(rtc, ((uint32_t)my_q * 32 + 8 * s + 4 * g) * 4);
+      qsn[s] = bload16(rts, ((uint32_t)my_q * 32 + 8 * s + 4 * g) * 4);
+    }
+  }
   wait_loads();
+  if (kRope) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qf[s][e] = rope_rotate<E>(qf[s][e], bits_to_float(qc[s][e]), bits_to_float(qsn[s][e]));
+    }
+  }
 
   f32x16_t oacc[2] = {zero16(), zero16()};  // O^T: rows d = 32*db + 8*(r/4) + 4g + r%4
   float m_run = -1e30f;                     // running max (base-2 units)
@@ -100,13 +121,23 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
 
   const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
   const uint32_t ld_off = (uint32_t)ld_row * kv_row + (uint32_t)kvh * kHeadDim * 2 + 2 * ld_col;
-  u32x4_t kreg, vreg;
+  u32x4_t kreg, vreg, kc, ksn;
   auto gload_tile = [&](int kt) {  // rows past the sequence end read as zero
     const uint32_t off = ld_off + (uint32_t)(kt * BN) * kv_row;
     kreg = bload16(rk, off);
     vreg = bload16(rv, off);
+    if (kRope) {  // pairs ld_col/2 + 0..3 of key row kt*BN + ld_row
+      const uint32_t toff = ((uint32_t)(kt * BN + ld_row) * 32 + ld_col / 2) * 4;
+      kc = bload16(rtc, toff);
+      ksn = bload16(rts, toff);
+    }
   };
   auto store_tile = [&](int buf) {
+    if (kRope) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        kreg[e] = rope_rotate<E>(kreg[e], bits_to_float(kc[e]), bits_to_float(ksn[e]));
+    }
     lds_store16(smem + (2 * buf) * TILE + ld_row * PITCH + ld_col, kreg);
     lds_store16(smem + (2 * buf + 1) * TILE + ld_row * PITCH + ld_col, vreg);
   };
@@ -233,27 +264,39 @@ const char* fwd_bf16_tiles() {
   return "fwd_bf16{BM=128,BN=64,waves=8(4 query x 2 key),mfma=32x32x16}";
 }
 
-template <class E>
-hipError_t launch_fwd_e(const Problem& p, const void* q, const void* k, const void* v, void* o,
-                           float* lse, hipStream_t s) {
+template <class E, bool kRope>
+hipError_t launch_fwd_e(const Problem& p, const void* q, const void* k, const void* v,
+                        const float* rcos, const float* rsin, void* o, float* lse, hipStream_t s) {
   const int n_qt = (p.T + BM - 1) / BM;
   const dim3 grid((unsigned)(n_qt * p.B * p.Hq));
-  auto kernel = p.scale_log2 >= 0.f ? attn_fwd_kernel<true, E> : attn_fwd_kernel<false, E>;
+  auto kernel = p.scale_log2 >= 0.f ? attn_fwd_kernel<true, E, kRope> : attn_fwd_kernel<false, E, kRope>;
   kernel<<<grid, NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, p.B, p.T, p.Hq, p.Hkv,
-      p.scale_log2, p.causal);
+      static_cast<const uint16_t*>(v), rcos, rsin, static_cast<uint16_t*>(o), lse, p.B, p.T, p.Hq,
+      p.Hkv, p.scale_log2, p.causal);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_rope_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                const float* rcos, const float* rsin, void* o, float* lse,
+                                hipStream_t s) {
+  return launch_fwd_e<Bf16, true>(p, q, k, v, rcos, rsin, o, lse, s);
+}
+
+hipError_t launch_fwd_rope_f16(const Problem& p, const void* q, const void* k, const void* v,
+                               const float* rcos, const float* rsin, void* o, float* lse,
+                               hipStream_t s) {
+  return launch_fwd_e<F16, true>(p, q, k, v, rcos, rsin, o, lse, s);
 }
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
                            float* lse, hipStream_t s) {
-  return launch_fwd_e<Bf16>(p, q, k, v, o, lse, s);
+  return launch_fwd_e<Bf16, false>(p, q, k, v, nullptr, nullptr, o, lse, s);
 }
 
 hipError_t launch_fwd_f16(const Problem& p, const void* q, const void* k, const void* v, void* o,
                            float* lse, hipStream_t s) {
-  return launch_fwd_e<F16>(p, q, k, v, o, lse, s);
+  return launch_fwd_e<F16, false>(p, q, k, v, nullptr, nullptr, o, lse, s);
 }
 
 }  // namespace rca

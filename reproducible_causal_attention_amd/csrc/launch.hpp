@@ -55,6 +55,31 @@ hipError_t launch_bwd_dq_f32(const Problem& p, const void* q, const void* k, con
                              const void* dO, const float* lse, const float* delta, void* dq,
                              hipStream_t s);
 
+// Rotary embedding (16-bit types; tables rcos, rsin: [T, 32] float32).  The
+// forward rotates q and k as it loads them; the backward's preparation writes
+// delta and the rotated q', k' (q_rot, k_rot), then the co-launched dK/dV + dQ
+// grid runs on q', k' and maps dq, dk back through the rotations.
+hipError_t launch_fwd_rope_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                                const float* rcos, const float* rsin, void* o, float* lse,
+                                hipStream_t s);
+hipError_t launch_fwd_rope_f16(const Problem& p, const void* q, const void* k, const void* v,
+                               const float* rcos, const float* rsin, void* o, float* lse,
+                               hipStream_t s);
+hipError_t launch_bwd_rope_prep_bf16(const Problem& p, const void* o, const void* dO, const void* q,
+                                     const void* k, const float* rcos, const float* rsin,
+                                     float* delta, void* q_rot, void* k_rot, hipStream_t s);
+hipError_t launch_bwd_rope_prep_f16(const Problem& p, const void* o, const void* dO, const void* q,
+                                    const void* k, const float* rcos, const float* rsin,
+                                    float* delta, void* q_rot, void* k_rot, hipStream_t s);
+hipError_t launch_bwd_dkdv_dq_rope_bf16(const Problem& p, const void* q_rot, const void* k_rot,
+                                        const void* v, const void* dO, const float* lse,
+                                        const float* delta, const float* rcos, const float* rsin,
+                                        void* dq, void* dk, void* dv, hipStream_t s);
+hipError_t launch_bwd_dkdv_dq_rope_f16(const Problem& p, const void* q_rot, const void* k_rot,
+                                       const void* v, const void* dO, const float* lse,
+                                       const float* delta, const float* rcos, const float* rsin,
+                                       void* dq, void* dk, void* dv, hipStream_t s);
+
 // Tile constants of each kernel family, reported by attn_build_info().
 const char* fwd_bf16_tiles();
 const char* bwd_dkdv_tiles();

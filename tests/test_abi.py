@@ -182,6 +182,78 @@ def test_step_entry_points_validate(lib):
                                 A.ATTN_BF16, None) == A.ATTN_ERR_INVALID_ARG
 
 
+def test_rope_workspace_bytes(lib):
+    f = lib.attn_bwd_rope_workspace_bytes
+    # delta (4*12*1024 float32) + q' (4*1024*12*64 bf16) + k' (4*1024*4*64 bf16)
+    assert f(4, 1024, 12, 4, 64, A.ATTN_BF16) == 4 * 12 * 1024 * 4 + 4 * 1024 * 12 * 128 + 4 * 1024 * 4 * 128
+    # 84 + 2688 + 896 bytes, each rounded up to 256
+    assert f(1, 7, 3, 1, 64, A.ATTN_F16) == 256 + 2816 + 1024
+    assert f(1, 7, 3, 1, 64, A.ATTN_F32) == 0    # rotary variants are 16-bit only
+    assert f(1, 7, 3, 2, 64, A.ATTN_BF16) == 0
+
+
+def fwd_rope_call(lib, **over):
+    a = dict(q=BASE, k=BASE + 16 * MB, v=BASE + 32 * MB, cos=BASE + 160 * MB, sin=BASE + 176 * MB,
+             o=BASE + 48 * MB, lse=BASE + 64 * MB, B=1, T=128, Hq=4, Hkv=2, D=64, scale=0.125,
+             causal=1, dtype=A.ATTN_BF16, stream=None)
+    a.update(over)
+    return lib.attn_fwd_rope(a["q"], a["k"], a["v"], a["cos"], a["sin"], a["o"], a["lse"], a["B"],
+                             a["T"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["dtype"],
+                             a["stream"])
+
+
+FWD_ROPE_ERRORS = [
+    ("f32", dict(dtype=A.ATTN_F32), A.ATTN_ERR_UNSUPPORTED),
+    ("null_cos", dict(cos=None), A.ATTN_ERR_INVALID_ARG),
+    ("misaligned_sin", dict(sin=BASE + 176 * MB + 4), A.ATTN_ERR_INVALID_ARG),
+    ("o_overlaps_cos", dict(o=BASE + 160 * MB + 128 * 32 * 4 - 16), A.ATTN_ERR_INVALID_ARG),
+    ("lse_overlaps_sin", dict(lse=BASE + 176 * MB), A.ATTN_ERR_INVALID_ARG),
+    ("head_dim_128", dict(D=128), A.ATTN_ERR_UNSUPPORTED),
+    ("groups_do_not_divide", dict(Hq=3), A.ATTN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,over,want", FWD_ROPE_ERRORS, ids=[e[0] for e in FWD_ROPE_ERRORS])
+def test_fwd_rope_validation(lib, name, over, want):
+    assert fwd_rope_call(lib, **over) == want
+
+
+def test_rope_tables_end_where_they_should(lib):
+    """o starting right after the cos table ([T, 32] float32) is not overlap; a
+    bad head dim makes the call fail after the overlap rule, so nothing launches."""
+    assert fwd_rope_call(lib, o=BASE + 160 * MB + 128 * 32 * 4, D=128) == A.ATTN_ERR_UNSUPPORTED
+
+
+def bwd_rope_call(lib, **over):
+    a = dict(q=BASE, k=BASE + 16 * MB, v=BASE + 32 * MB, o=BASE + 48 * MB, lse=BASE + 64 * MB,
+             dO=BASE + 80 * MB, cos=BASE + 160 * MB, sin=BASE + 176 * MB, dq=BASE + 96 * MB,
+             dk=BASE + 112 * MB, dv=BASE + 128 * MB, B=1, T=128, Hq=4, Hkv=2, D=64, scale=0.125,
+             causal=1, dtype=A.ATTN_BF16, ws=BASE + 144 * MB, ws_bytes=None, stream=None)
+    a.update(over)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.attn_bwd_rope_workspace_bytes(1, 128, 4, 2, 64, A.ATTN_BF16)
+    return lib.attn_bwd_rope(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["cos"], a["sin"],
+                             a["dq"], a["dk"], a["dv"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                             a["scale"], a["causal"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+BWD_ROPE_ERRORS = [
+    ("f32", dict(dtype=A.ATTN_F32), A.ATTN_ERR_UNSUPPORTED),
+    ("workspace_too_small", dict(ws_bytes=512 + 65536 + 32768 - 1), A.ATTN_ERR_INVALID_ARG),
+    ("plain_bwd_workspace_is_too_small", dict(ws_bytes=4 * 128 * 4), A.ATTN_ERR_INVALID_ARG),
+    ("null_sin", dict(sin=None), A.ATTN_ERR_INVALID_ARG),
+    ("workspace_overlaps_cos", dict(ws=BASE + 160 * MB - 65536), A.ATTN_ERR_INVALID_ARG),
+    ("dk_overlaps_sin", dict(dk=BASE + 176 * MB + 256), A.ATTN_ERR_INVALID_ARG),
+    ("scale_inf", dict(scale=float("inf")), A.ATTN_ERR_INVALID_ARG),
+    ("head_dim_32", dict(D=32), A.ATTN_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,over,want", BWD_ROPE_ERRORS, ids=[e[0] for e in BWD_ROPE_ERRORS])
+def test_bwd_rope_validation(lib, name, over, want):
+    assert bwd_rope_call(lib, **over) == want
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
