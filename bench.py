@@ -24,7 +24,11 @@ The cpu_baseline leg times the fp64 numpy oracle on a bounded sample of
 (batch, KV-group) units of the same workload on the host cores, and compares
 its outputs with the GPU's on those units.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With ``--rope`` the step is the rotary variant instead: attn_fwd_rope, then
+attn_bwd_rope (its preparation kernel -- delta and the rotated q', k' -- and the
+co-launched dK/dV + dQ grid on q', k'), with cos / sin tables of base 10000.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rope]
 Prints one JSON line on stdout.
 """
 from __future__ import annotations
@@ -84,9 +88,12 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle cpu_baseline sample (0: skip)")
     ap.add_argument("--kernel-only", default=None,
-                    choices=("fwd", "bwd_preprocess", "bwd_dkdv_dq", "bwd_dkdv", "bwd_dq"),
+                    choices=("fwd", "bwd_preprocess", "bwd_dkdv_dq", "bwd_dkdv", "bwd_dq",
+                             "fwd_rope", "bwd_rope"),
                     help="counter runs: launch only this kernel --launches times and exit")
     ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--rope", action="store_true",
+                    help="time the rotary-embedding variant (attn_fwd_rope + attn_bwd_rope)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="counter calibration: copy this many bytes device to device "
                          "--launches times and exit")
@@ -149,6 +156,13 @@ def main() -> int:
 
     names = ("fwd", "bwd_preprocess", "bwd_dkdv_dq")  # one step, in order
     all_names = names + ("bwd_dkdv", "bwd_dq")
+    rope = None
+    if args.rope:
+        names = all_names = ("fwd_rope", "bwd_rope")
+        c_np, s_np = W.rope_tables(T, D)
+        ws_bytes = int(lib.attn_bwd_rope_workspace_bytes(B, T, Hq, Hkv, D, bf))
+        rope = {"cos": torch.from_numpy(c_np).to(dev), "sin": torch.from_numpy(s_np).to(dev),
+                "ws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev), "np": (c_np, s_np)}
 
     def kernel(name, x, b):
         qq, kk, vv, dd = x
@@ -167,10 +181,20 @@ def main() -> int:
             launch("attn_bwd_dkdv", qq.data_ptr(), kk.data_ptr(), vv.data_ptr(), dd.data_ptr(),
                    b["lse"].data_ptr(), b["delta"].data_ptr(), b["dk"].data_ptr(),
                    b["dv"].data_ptr(), B, T, Hq, Hkv, D, w.scale, causal, bf, s)
-        else:
+        elif name == "bwd_dq":
             launch("attn_bwd_dq", qq.data_ptr(), kk.data_ptr(), vv.data_ptr(), dd.data_ptr(),
                    b["lse"].data_ptr(), b["delta"].data_ptr(), b["dq"].data_ptr(),
                    B, T, Hq, Hkv, D, w.scale, causal, bf, s)
+        elif name == "fwd_rope":
+            launch("attn_fwd_rope", qq.data_ptr(), kk.data_ptr(), vv.data_ptr(),
+                   rope["cos"].data_ptr(), rope["sin"].data_ptr(), b["o"].data_ptr(),
+                   b["lse"].data_ptr(), B, T, Hq, Hkv, D, w.scale, causal, bf, s)
+        else:  # bwd_rope: preparation kernel, then the co-launched dK/dV + dQ grid
+            launch("attn_bwd_rope", qq.data_ptr(), kk.data_ptr(), vv.data_ptr(),
+                   b["o"].data_ptr(), b["lse"].data_ptr(), dd.data_ptr(), rope["cos"].data_ptr(),
+                   rope["sin"].data_ptr(), b["dq"].data_ptr(), b["dk"].data_ptr(),
+                   b["dv"].data_ptr(), B, T, Hq, Hkv, D, w.scale, causal, bf,
+                   rope["ws"].data_ptr(), rope["ws"].numel(), s)
 
     def step(x, bufs, mark=None, ev=None):
         """One fwd+bwd step; with mark set, events ev[0], ev[1] bracket that kernel."""
@@ -206,7 +230,8 @@ def main() -> int:
         step((q, k, v, dO), bufs)
         torch.cuda.synchronize()
         hashes.append(digest(bufs))
-    gate = {"finite": all(bool(torch.isfinite(bufs[n].float()).all()) for n in bufs),
+    outs = ("o", "lse", "dq", "dk", "dv") + (() if rope else ("delta",))  # rotary: delta in the workspace
+    gate = {"finite": all(bool(torch.isfinite(bufs[n].float()).all()) for n in outs),
             "hash_repeats_equal": len(set(hashes)) == 1}
     G = Hq // Hkv
     dv32, dk32, dO32 = bufs["dv"].float(), bufs["dk"].float(), dO.float()
@@ -214,7 +239,13 @@ def main() -> int:
     want = dO32.view(B, T, Hkv, G, D).sum(dim=(1, 3))
     got = dv32.sum(dim=1)
     gate["dv_column_sum_rel_err"] = float((got - want).abs().max() / want.abs().max())
-    # Key-translation invariance: sum_j dk_j = 0, relative to the column sums of |dk|.
+    # Key-translation invariance: sum_j dk_j = 0, relative to the column sums of |dk|
+    # (with rotary positions it holds for the gradients of the rotated keys, so
+    # each dk_j is rotated forward by its position's angles first).
+    if rope is not None:
+        cs, sn = rope["cos"][None, :, None, :], rope["sin"][None, :, None, :]
+        a, b_ = dk32[..., 0::2], dk32[..., 1::2]
+        dk32 = torch.stack((a * cs - b_ * sn, a * sn + b_ * cs), dim=-1).flatten(-2)
     gate["dk_sum_rel"] = float(dk32.sum(dim=1).abs().max() / dk32.abs().sum(dim=1).max())
     gate["ok"] = (gate["finite"] and gate["hash_repeats_equal"]
                   and gate["dv_column_sum_rel_err"] < 2e-2 and gate["dk_sum_rel"] < 2e-2)
@@ -277,6 +308,8 @@ def main() -> int:
         "bwd_dkdv": 8.0 * D * pairs,   # S, dP, dV, dK
         "bwd_dq": 6.0 * D * pairs,     # S and dP recomputed, dQ
         "bwd_preprocess": 2.0 * B * T * Hq * D * 2 + 4.0 * B * Hq * T,
+        "fwd_rope": 4.0 * D * pairs,
+        "bwd_rope": 10.0 * D * pairs,  # two launches: preparation + dK/dV + dQ grid
     }
     sec = dom_us * 1e-6
     src_digest = kernel_sources_digest()
@@ -292,13 +325,17 @@ def main() -> int:
     roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(dom_us, 2)
-    if dom == "bwd_dkdv_dq":  # matrix work the split design executes (S and dP twice)
+    if dom in ("bwd_dkdv_dq", "bwd_rope"):  # matrix work the split design executes (S and dP twice)
         roof["executed_tflops"] = round(14.0 * D * pairs / sec / 1e12, 1)
-    pre_gbs = algo["bwd_preprocess"] / (per_kernel_us["bwd_preprocess"] * 1e-6) / 1e9
+    if dom == "bwd_rope":
+        roof["note"] = ("attn_bwd_rope as a whole: its preparation kernel and the co-launched "
+                        "dK/dV + dQ grid, between one pair of events")
+    pre_gbs = (algo["bwd_preprocess"] / (per_kernel_us["bwd_preprocess"] * 1e-6) / 1e9
+               if "bwd_preprocess" in per_kernel_us else None)
 
     # ---- a stack of independent layers (forward 0..L-1, backward L-1..0) ----
     layers = None
-    if args.layers > 0:
+    if args.layers > 0 and rope is None:
         L = args.layers
         xs = [(torch.randn_like(q, dtype=torch.float32).to(tdt),
                torch.randn_like(k, dtype=torch.float32).to(tdt),
@@ -342,7 +379,7 @@ def main() -> int:
     # ---- cpu_baseline: the oracle on a bounded sample of the same workload ----
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, inp, bufs, args.cpu_seconds)
+        cpu = cpu_baseline(w, inp, bufs, args.cpu_seconds, rope["np"] if rope else None)
         log("cpu_baseline", cpu)
 
     out = {
@@ -358,13 +395,14 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D,
-                   "causal": bool(w.causal), "scale": w.scale,
-                   "gflop_per_step": round(flops / 1e9, 4)},
+        "config": {"workload": w.name + ("+rope" if rope else ""), "B": B, "T": T, "Hq": Hq,
+                   "Hkv": Hkv, "D": D, "causal": bool(w.causal), "scale": w.scale,
+                   "gflop_per_step": round(flops / 1e9, 4),
+                   **({"rope": {"pairs": "adjacent", "base": 10000.0}} if rope else {})},
         "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "per_kernel_us": {n: round(u, 2) for n, u in per_kernel_us.items()},
         "event_step_us": round(event_step_us, 2),
-        "preprocess_gbs": round(pre_gbs, 1),
+        "preprocess_gbs": round(pre_gbs, 1) if pre_gbs is not None else None,
         "roofline": roof,
         "cpu_baseline": cpu,
         "layers": layers,
@@ -380,9 +418,10 @@ def main() -> int:
     return 0
 
 
-def cpu_baseline(w, inp, bufs, budget_s):
+def cpu_baseline(w, inp, bufs, budget_s, tables=None):
     """Time the fp64 oracle on (batch, KV-group) units until ``budget_s`` is spent,
-    and compare the GPU outputs of those units with it."""
+    and compare the GPU outputs of those units with it.  With rotary ``tables``
+    (cos, sin) the oracle rotates q and k first (timed) and maps dq, dk back."""
     import numpy as np
 
     import oracle
@@ -393,6 +432,11 @@ def cpu_baseline(w, inp, bufs, budget_s):
     except Exception:  # threadpoolctl missing or unusable
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     q, k, v, dO = (inp.as_float64(n) for n in ("q", "k", "v", "dO"))
+    rot_secs = 0.0
+    if tables is not None:
+        t0 = time.perf_counter()
+        q, k = oracle.apply_rope(q, *tables), oracle.apply_rope(k, *tables)
+        rot_secs = time.perf_counter() - t0
     gpu = {n: bufs[n].float().cpu().numpy().astype(np.float64) for n in ("o", "lse", "dq", "dk", "dv")}
     units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     G = w.G
@@ -401,6 +445,9 @@ def cpu_baseline(w, inp, bufs, budget_s):
         t0 = time.perf_counter()
         o_r, lse_r = oracle.ref_fwd_group(q, k, v, w.scale, w.causal, b, g)
         dq_r, dk_r, dv_r, _ = oracle.ref_bwd_group(q, k, v, dO, w.scale, w.causal, b, g)
+        if tables is not None:
+            dq_r = oracle.apply_rope_transpose(dq_r[None], *tables)[0]
+            dk_r = oracle.apply_rope_transpose(dk_r[None, :, None], *tables)[0, :, 0]
         secs += time.perf_counter() - t0
         done += 1
         hs = slice(g * G, (g + 1) * G)
@@ -411,11 +458,13 @@ def cpu_baseline(w, inp, bufs, budget_s):
         worst["lse"] = max(worst.get("lse", 0.0), float(np.max(np.abs(gpu["lse"][b, hs] - lse_r))))
         if secs >= budget_s:
             break
+    secs += rot_secs * done / len(units)  # this sample's share of the rotation
     pairs_per_unit = G * (w.T * (w.T + 1) // 2 if w.causal else w.T * w.T)
     flops = done * pairs_per_unit * (4.0 + 10.0) * w.D
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} of {len(units)} (batch, KV-group) units of {w.name}, fwd+bwd, "
+            "sample": f"{done} of {len(units)} (batch, KV-group) units of {w.name}"
+                      f"{' with rotary positions' if tables is not None else ''}, fwd+bwd, "
                       f"{secs:.2f} s",
             "seconds": round(secs, 3),
             "max_err_vs_gpu": {n: float(f"{e:.3g}") for n, e in worst.items()},
