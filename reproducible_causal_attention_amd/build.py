@@ -1,8 +1,10 @@
-"""Ahead-of-time build of libattn.so for gfx950 with hipcc (no JIT, no torch extension).
+"""Ahead-of-time build of the libraries for gfx950 with hipcc (no JIT, no torch extension).
 
 ``python -m reproducible_causal_attention_amd.build`` or ``build()`` compiles every
-HIP source under ``csrc/`` into ``libattn.so`` next to this file.  The library is
-always rebuilt, so a stale binary never survives a source change.
+HIP source directly under ``csrc/`` into ``libattn.so`` (the fused path) and the
+sources under ``csrc/unfused/`` into ``libattn_unfused.so`` (the unfused
+baseline, linked against rocBLAS), next to this file.  Both are always rebuilt,
+so a stale binary never survives a source change.
 """
 from __future__ import annotations
 
@@ -15,6 +17,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
+UNFUSED_LIB_PATH = os.path.join(PKG_DIR, "libattn_unfused.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -45,11 +48,14 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = True) -> str:
-    """Compile libattn.so; raises ``RuntimeError`` with the compiler output on failure."""
-    tmp = LIB_PATH + ".tmp"
+def unfused_sources():
+    return sorted(glob.glob(os.path.join(CSRC, "unfused", "*.hip")))
+
+
+def _compile(srcs, out, extra, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, *HIP_FLAGS, f'-DATTN_GIT_REV="{_revision()}"',
-           f"-I{os.path.join(ROOT, 'include')}", *sources(), "-o", tmp]
+           f"-I{os.path.join(ROOT, 'include')}", *srcs, *extra, "-o", tmp]
     if verbose:
         print("[build]", " ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,7 +65,15 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, flush=True)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = True) -> str:
+    """Compile libattn.so and libattn_unfused.so; raises ``RuntimeError`` with the
+    compiler output on failure.  Returns the path of libattn.so."""
+    _compile(sources(), LIB_PATH, [], verbose)
+    _compile(unfused_sources(), UNFUSED_LIB_PATH, ["-L/opt/rocm/lib", "-lrocblas"], verbose)
     return LIB_PATH
 
 

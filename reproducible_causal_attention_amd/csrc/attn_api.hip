@@ -8,6 +8,7 @@
 
 #include "../../include/attn.h"
 #include "launch.hpp"
+#include "validate.hpp"
 
 #define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -17,25 +18,12 @@
 
 namespace {
 
+using namespace rca::validate;
+
 constexpr long long kMaxT = 1LL << 24;
 constexpr long long kMaxTiles = 1LL << 23;     // ceil(T/64) * B * Hq
 constexpr long long kMaxElements = 1LL << 40;  // per tensor
 constexpr long long kMaxBatchBytes = 1LL << 31; // one batch element of any tensor (buffer offsets are 32-bit)
-
-struct Span {
-  uintptr_t lo, hi;
-};
-
-Span span_of(const void* p, size_t bytes) {
-  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return Span{lo, lo + bytes};
-}
-
-bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-size_t elem_size(attn_dtype_t dt) { return dt == ATTN_F32 ? 4 : 2; }
 
 // Sizes and dtype, shared by every entry point (Hkv = Hq where no KV tensor is involved).
 attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype) {
@@ -48,31 +36,6 @@ attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dty
   if ((long long)T * Hq * (long long)D * 4 >= kMaxBatchBytes) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
   if (D != rca::kHeadDim) return ATTN_ERR_UNSUPPORTED;
-  return ATTN_OK;
-}
-
-attn_status_t check_scalars(float scale, int causal) {
-  if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
-  return ATTN_OK;
-}
-
-// Null and alignment checks over a list of pointers.
-attn_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
-  for (const void* p : ptrs) {
-    if (p == nullptr || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
-  }
-  return ATTN_OK;
-}
-
-// No output may overlap an input or another output.
-attn_status_t check_disjoint(std::initializer_list<Span> inputs, std::initializer_list<Span> outputs) {
-  for (auto o = outputs.begin(); o != outputs.end(); ++o) {
-    for (const Span& i : inputs)
-      if (overlap(*o, i)) return ATTN_ERR_INVALID_ARG;
-    for (auto o2 = o + 1; o2 != outputs.end(); ++o2)
-      if (overlap(*o, *o2)) return ATTN_ERR_INVALID_ARG;
-  }
   return ATTN_OK;
 }
 
@@ -100,8 +63,6 @@ void discard_stale_error() { (void)hipGetLastError(); }
 attn_status_t check_rope_dtype(attn_dtype_t dtype) {
   return dtype == ATTN_BF16 || dtype == ATTN_F16 ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
 }
-
-size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 #define ATTN_TRY(expr)                       \
   do {                                       \
