@@ -28,7 +28,13 @@ With ``--rope`` the step is the rotary variant instead: attn_fwd_rope, then
 attn_bwd_rope (its preparation kernel -- delta and the rotated q', k' -- and the
 co-launched dK/dV + dQ grid on q', k'), with cos / sin tables of base 10000.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rope]
+With ``--unfused`` the step is the unfused baseline of libattn_unfused.so
+(attn_unfused_fwd + attn_unfused_bwd: float32 [T, T] scores from rocBLAS GEMMs
+and the three softmax row kernels); its roofline object covers the dominant
+row kernel against HBM bandwidth, each row kernel timed alone by HIP events
+around back-to-back launches on the step's buffers.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rope | --unfused]
 Prints one JSON line on stdout.
 """
 from __future__ import annotations
@@ -92,6 +98,8 @@ def main() -> int:
                              "fwd_rope", "bwd_rope"),
                     help="counter runs: launch only this kernel --launches times and exit")
     ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused baseline (libattn_unfused.so) instead")
     ap.add_argument("--rope", action="store_true",
                     help="time the rotary-embedding variant (attn_fwd_rope + attn_bwd_rope)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -125,6 +133,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copied {args.copy_bytes} bytes x {args.launches}")
         return 0
+    if args.unfused:
+        return main_unfused(args)
     lib = A.load_library()
     w = W.WORKLOADS[args.workload]
     if w.dtype not in ("bf16", "f16"):
@@ -415,6 +425,174 @@ def main() -> int:
     print(json.dumps(out), flush=True)
     if cpu is not None and not cpu.get("parity_ok", True):
         return 1
+    return 0
+
+
+def row_kernel_bytes(name, B, T, Hq, causal):
+    """Algorithmic HBM bytes of one launch of an unfused row kernel: the visible
+    part of each row read (float32 scores / dP, 16-bit P), every column of the
+    16-bit output written, float32 lse read or written."""
+    vis = B * Hq * (T * (T + 1) // 2 if causal else T * T)
+    full = B * Hq * T * T
+    rows = B * Hq * T
+    return {"softmax_lse": 4 * vis + 2 * full + 4 * rows,
+            "probs_from_lse": 4 * vis + 4 * rows + 2 * full,
+            "softmax_bwd": (2 + 4) * vis + 2 * full}[name]
+
+
+def main_unfused(args) -> int:
+    """The unfused baseline's step: attn_unfused_fwd + attn_unfused_bwd."""
+    import numpy as np
+    import torch
+
+    from reproducible_causal_attention_amd import attn as A
+    from reproducible_causal_attention_amd import unfused as U
+    from reproducible_causal_attention_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    if w.dtype not in ("bf16", "f16"):
+        print("the unfused baseline runs bf16 and f16 workloads", file=sys.stderr)
+        return 2
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
+    dev = torch.device("cuda:0")
+    lib = U.load_library()
+    code = A.ATTN_BF16 if w.dtype == "bf16" else A.ATTN_F16
+    log("unfused baseline", w.name, w.label())
+    inp = W.generate(w)
+    q, k, v, dO = (torch.from_numpy(getattr(inp, n).view(np.int16)).view(tdt).to(dev)
+                   for n in ("q", "k", "v", "dO"))
+    ws = torch.empty(int(lib.attn_unfused_workspace_bytes(B, T, Hq, Hkv, D, code)),
+                     dtype=torch.uint8, device=dev)
+    bufs = dict(o=torch.empty_like(q), lse=torch.empty((B, Hq, T), device=dev),
+                dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
+    # row-kernel operands of their own, [B, Hq, T, T]
+    n = B * Hq * T * T
+    rows = dict(s=torch.randn(n, device=dev), dp=torch.randn(n, device=dev),
+                p=torch.empty(n, dtype=tdt, device=dev), ds=torch.empty(n, dtype=tdt, device=dev),
+                lse=torch.empty(B * Hq * T, device=dev))
+    ctx = U.Context()
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    causal = int(w.causal)
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {A.load_library().attn_status_string(st).decode()}")
+
+    def kernel(name):
+        if name == "unfused_fwd":
+            check(lib.attn_unfused_fwd(ctx.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       bufs["o"].data_ptr(), bufs["lse"].data_ptr(), B, T, Hq, Hkv,
+                                       D, w.scale, causal, code, ws.data_ptr(), ws.numel(), s), name)
+        elif name == "unfused_bwd":
+            check(lib.attn_unfused_bwd(ctx.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       bufs["lse"].data_ptr(), dO.data_ptr(), bufs["dq"].data_ptr(),
+                                       bufs["dk"].data_ptr(), bufs["dv"].data_ptr(), B, T, Hq, Hkv,
+                                       D, w.scale, causal, code, ws.data_ptr(), ws.numel(), s), name)
+        elif name == "softmax_lse":
+            check(lib.attn_unfused_softmax_lse(rows["s"].data_ptr(), rows["p"].data_ptr(),
+                                               rows["lse"].data_ptr(), B * Hq * T, T, w.scale,
+                                               causal, code, s), name)
+        elif name == "probs_from_lse":
+            check(lib.attn_unfused_probs_from_lse(rows["s"].data_ptr(), rows["lse"].data_ptr(),
+                                                  rows["p"].data_ptr(), B * Hq * T, T, w.scale,
+                                                  causal, code, s), name)
+        else:
+            check(lib.attn_unfused_softmax_bwd(rows["p"].data_ptr(), rows["dp"].data_ptr(),
+                                               rows["ds"].data_ptr(), B * Hq * T, T, causal, code,
+                                               s), name)
+
+    names = ("unfused_fwd", "unfused_bwd")
+    row_names = ("softmax_lse", "probs_from_lse", "softmax_bwd")
+
+    def digest():
+        h = hashlib.sha256()
+        for nme in ("o", "lse", "dq", "dk", "dv"):
+            h.update(bufs[nme].contiguous().view(torch.uint8).cpu().numpy().tobytes())
+        return h.hexdigest()
+
+    hashes = []
+    for _ in range(3):
+        for nme in names:
+            kernel(nme)
+        torch.cuda.synchronize()
+        hashes.append(digest())
+    gate = {"finite": all(bool(torch.isfinite(bufs[nme].float()).all()) for nme in bufs),
+            "hash_repeats_equal": len(set(hashes)) == 1}
+    gate["ok"] = gate["finite"] and gate["hash_repeats_equal"]
+    log("gate", gate)
+    if not gate["ok"]:
+        print(json.dumps({"metric": "gate failed", "gate": gate}), flush=True)
+        return 1
+    for nme in row_names:  # warm the row operands (p from s, etc.)
+        kernel(nme)
+    for _ in range(args.warmup):
+        for nme in names:
+            kernel(nme)
+    torch.cuda.synchronize()
+
+    per_kernel_us = {}
+    n_rep = max(5, min(20, args.steps // 4))
+    for nme in names + row_names:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2e6))
+        e0.record(stream)
+        for _ in range(n_rep):
+            kernel(nme)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_kernel_us[nme] = 1e3 * e0.elapsed_time(e1) / n_rep
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for nme in names:
+            kernel(nme)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    flops = w.fwd_flops + w.bwd_flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    dom = max(row_names, key=per_kernel_us.get)
+    nbytes = row_kernel_bytes(dom, B, T, Hq, bool(causal))
+    achieved = nbytes / (per_kernel_us[dom] * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+            "avg_launch_us": round(per_kernel_us[dom], 2), "bytes_per_launch": nbytes,
+            "timing": "back-to-back launches of the row kernel alone between HIP events"}
+    row_gbs = {nme: round(row_kernel_bytes(nme, B, T, Hq, bool(causal)) / (per_kernel_us[nme] * 1e-6) / 1e9, 1)
+               for nme in row_names}
+    log(f"unfused step {ms_per_step * 1e3:.1f} us, {tflops:.1f} TFLOP/s; kernels {per_kernel_us}; "
+        f"row kernels GB/s {row_gbs}")
+    ctx.close()
+    out = {
+        "metric": "attn fwd+bwd TFLOP/s & % bf16 MFMA peak, B4·T1024 GQA12/4 d64",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name + "+unfused", "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D,
+                   "causal": bool(w.causal), "scale": w.scale,
+                   "gflop_per_step": round(flops / 1e9, 4),
+                   "path": "unfused baseline: [T,T] float32 scores in HBM, rocBLAS GEMMs"},
+        "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "per_kernel_us": {nme: round(u, 2) for nme, u in per_kernel_us.items()},
+        "row_kernel_gbs": row_gbs,
+        "roofline": roof,
+        "cpu_baseline": None,
+        "gate": gate,
+        "output_sha256": hashes[0],
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
     return 0
 
 

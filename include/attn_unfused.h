@@ -16,16 +16,17 @@
  *             in the input dtype and lse;  o = P v (GEMM).
  *   backward: S = q k^T again;  probs_from_lse: P from S and lse;  dP = dO v^T
  *             (GEMM, float32);  softmax_bwd: dS = P (dP - sum_j P dP) in the input
- *             dtype;  dv = sum over the group's heads of P^T dO, dk = scale sum
- *             dS^T q (GEMMs accumulated in float32 in a fixed head order, then
- *             rounded);  dq = scale dS k (GEMM).
+ *             dtype;  per query head P^T dO and scale dS^T q (GEMMs, float32),
+ *             summed over each KV group's heads in a fixed order and rounded to
+ *             dv and dk;  dq = scale dS k (GEMM).
  * With causal = 1 the row kernels read only the visible part of each row and
  * write zeros past it; the GEMMs run over the whole matrix.
  *
- * GEMMs are rocBLAS strided-batched GEMMs (inputs in the 16-bit type, float32
- * accumulation) with atomics disallowed, so the results are bitwise run-to-run
- * reproducible on one device like the fused library's; every reduction in the
- * row kernels has a fixed order.
+ * GEMMs are rocBLAS strided-batched GEMMs over the query heads of each batch
+ * element (k and v first repeated to the query heads; inputs in the 16-bit
+ * type, float32 accumulation) with atomics disallowed, so the results are
+ * bitwise run-to-run reproducible on one device like the fused library's; every
+ * reduction in the library's own kernels has a fixed order.
  *
  * Unlike libattn.so this library holds state: a context owns a rocBLAS handle
  * (which allocates device memory of its own).  A context may be used by one
@@ -54,8 +55,9 @@ attn_status_t attn_unfused_create(attn_unfused_ctx** ctx);
 void attn_unfused_destroy(attn_unfused_ctx* ctx);
 
 /* Workspace bytes for attn_unfused_fwd and attn_unfused_bwd: float32 S / dP and
- * 16-bit P and dS, each [B, Hq, T, T], then float32 dk and dv accumulators
- * [B, T, Hkv, D], each rounded up to 256 bytes.  0 for invalid sizes. */
+ * 16-bit P and dS, each [B, Hq, T, T]; float32 per-query-head dk and dv partials,
+ * each [B, Hq, T, D]; then k and v repeated to the query heads, 16-bit
+ * [B, T, Hq, D] each; each part rounded up to 256 bytes.  0 for invalid sizes. */
 size_t attn_unfused_workspace_bytes(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype);
 
 /* Forward: o and lse as attn_fwd.  The workspace is clobbered. */

@@ -207,66 +207,199 @@ __global__ __launch_bounds__(kThreads) void softmax_bwd_kernel(const uint16_t* _
   }
 }
 
-// float32 -> 16-bit type, element by element (the dK and dV accumulators).
-template <class E>
-__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ x,
-                                                       uint16_t* __restrict__ y, long long n) {
-  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i + 3 < n) {
-    const float4 v = *reinterpret_cast<const float4*>(x + i);
-    u32x2_t w;
-    w[0] = E::pack2(v.x, v.y);
-    w[1] = E::pack2(v.z, v.w);
-    *reinterpret_cast<u32x2_t*>(y + i) = w;
-  } else {
-    for (long long j = i; j < n; ++j) y[j] = to_e16<E>(x[j]);
+// Register-resident variants for T % 4 == 0 and T <= 256*CH: lane l holds
+// columns 4l + 256c + 0..3 of its row for c < CH, so every load of the row is
+// issued before the first use and each row is read from HBM once.
+template <int CH>
+__device__ __forceinline__ void load_row_f32(const float* __restrict__ src, int len, int lane,
+                                             float (&x)[CH][4], float fill) {
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int j0 = 4 * lane + 256 * c;
+    if (j0 + 3 < len) {
+      const float4 v = *reinterpret_cast<const float4*>(src + j0);
+      x[c][0] = v.x; x[c][1] = v.y; x[c][2] = v.z; x[c][3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[c][e] = j0 + e < len ? src[j0 + e] : fill;
+    }
   }
+}
+
+template <class E, int CH>
+__device__ __forceinline__ void store_row_e16(uint16_t* __restrict__ dst, int T, int lane,
+                                              const float (&y)[CH][4]) {
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int j0 = 4 * lane + 256 * c;
+    if (j0 < T) {  // T % 4 == 0: the whole group of four is in the row
+      u32x2_t w;
+      w[0] = E::pack2(y[c][0], y[c][1]);
+      w[1] = E::pack2(y[c][2], y[c][3]);
+      *reinterpret_cast<u32x2_t*>(dst + j0) = w;
+    }
+  }
+}
+
+template <class E, int CH>
+__global__ __launch_bounds__(kThreads) void softmax_lse_resident(const float* __restrict__ s,
+                                                                  uint16_t* __restrict__ p,
+                                                                  float* __restrict__ lse,
+                                                                  long long n_rows, int T,
+                                                                  float scale_log2, int causal) {
+  Row r;
+  if (!row_of(n_rows, T, causal, r)) return;
+  const int lane = threadIdx.x & 63;
+  float x[CH][4];
+  load_row_f32<CH>(s + r.base, r.len, lane, x, 0.f);
+  float m = -1e30f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = 4 * lane + 256 * c + e < r.len;
+      x[c][e] = in ? x[c][e] * scale_log2 : -1e30f;
+      m = fmaxf(m, x[c][e]);
+    }
+  float l = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l += fast_exp2(x[c][e] - m);
+  wave_merge(m, l);
+  const float lse2 = m + fast_log2(l);
+  if (lane == 0) lse[r.base / (size_t)T] = lse2 * kLn2;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x[c][e] = 4 * lane + 256 * c + e < r.len ? fast_exp2(x[c][e] - lse2) : 0.f;
+  store_row_e16<E, CH>(p + r.base, T, lane, x);
+}
+
+template <class E, int CH>
+__global__ __launch_bounds__(kThreads) void probs_from_lse_resident(const float* __restrict__ s,
+                                                                     const float* __restrict__ lse,
+                                                                     uint16_t* __restrict__ p,
+                                                                     long long n_rows, int T,
+                                                                     float scale_log2, int causal) {
+  Row r;
+  if (!row_of(n_rows, T, causal, r)) return;
+  const int lane = threadIdx.x & 63;
+  const float lse2 = lse[r.base / (size_t)T] * kLog2e;
+  float x[CH][4];
+  load_row_f32<CH>(s + r.base, r.len, lane, x, 0.f);
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x[c][e] = 4 * lane + 256 * c + e < r.len ? fast_exp2(x[c][e] * scale_log2 - lse2) : 0.f;
+  store_row_e16<E, CH>(p + r.base, T, lane, x);
+}
+
+template <class E, int CH>
+__global__ __launch_bounds__(kThreads) void softmax_bwd_resident(const uint16_t* __restrict__ p,
+                                                                  const float* __restrict__ dp,
+                                                                  uint16_t* __restrict__ ds,
+                                                                  long long n_rows, int T,
+                                                                  int causal) {
+  Row r;
+  if (!row_of(n_rows, T, causal, r)) return;
+  const int lane = threadIdx.x & 63;
+  float g[CH][4], pv[CH][4];
+  load_row_f32<CH>(dp + r.base, r.len, lane, g, 0.f);
+  const uint16_t* pr = p + r.base;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int j0 = 4 * lane + 256 * c;
+    if (j0 + 3 < r.len) {
+      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(pr + j0);
+      pv[c][0] = E::lo(w[0]); pv[c][1] = E::hi(w[0]);
+      pv[c][2] = E::lo(w[1]); pv[c][3] = E::hi(w[1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[c][e] = j0 + e < r.len ? from_e16<E>(pr[j0 + e]) : 0.f;
+    }
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(pv[c][e], g[c][e], acc);
+  const float delta = wave_sum(acc);
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[c][e] = pv[c][e] * (g[c][e] - delta);  // 0 past len
+  store_row_e16<E, CH>(ds + r.base, T, lane, g);
 }
 
 dim3 row_grid(long long n_rows) { return dim3((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock)); }
 
 }  // namespace
 
+
+// Chunks per lane of the register-resident kernels: 1, 2, 4 or 8 (T <= 2048,
+// T % 4 == 0), else 0 (the looped kernels).
+int resident_chunks(int T) {
+  if (T % 4 != 0 || T > 2048) return 0;
+  return T <= 256 ? 1 : T <= 512 ? 2 : T <= 1024 ? 4 : 8;
+}
+
+#define RCA_RESIDENT_DISPATCH(KERNEL, ...)                                                  \
+  switch (resident_chunks(T)) {                                                            \
+    case 1: KERNEL<E, 1><<<row_grid(n_rows), kThreads, 0, st>>>(__VA_ARGS__); break;      \
+    case 2: KERNEL<E, 2><<<row_grid(n_rows), kThreads, 0, st>>>(__VA_ARGS__); break;      \
+    case 4: KERNEL<E, 4><<<row_grid(n_rows), kThreads, 0, st>>>(__VA_ARGS__); break;      \
+    default: KERNEL<E, 8><<<row_grid(n_rows), kThreads, 0, st>>>(__VA_ARGS__); break;     \
+  }
+
 template <class E>
 hipError_t softmax_lse(const float* s, void* p, float* lse, long long n_rows, int T,
                        float scale_log2, int causal, hipStream_t st) {
-  if (T % 4 == 0)
-    softmax_lse_kernel<E, 4><<<row_grid(n_rows), kThreads, 0, st>>>(
-        s, static_cast<uint16_t*>(p), lse, n_rows, T, scale_log2, causal);
-  else
-    softmax_lse_kernel<E, 1><<<row_grid(n_rows), kThreads, 0, st>>>(
-        s, static_cast<uint16_t*>(p), lse, n_rows, T, scale_log2, causal);
+  uint16_t* p16 = static_cast<uint16_t*>(p);
+  if (resident_chunks(T) > 0) {
+    RCA_RESIDENT_DISPATCH(softmax_lse_resident, s, p16, lse, n_rows, T, scale_log2, causal)
+  } else if (T % 4 == 0) {
+    softmax_lse_kernel<E, 4><<<row_grid(n_rows), kThreads, 0, st>>>(s, p16, lse, n_rows, T,
+                                                                     scale_log2, causal);
+  } else {
+    softmax_lse_kernel<E, 1><<<row_grid(n_rows), kThreads, 0, st>>>(s, p16, lse, n_rows, T,
+                                                                     scale_log2, causal);
+  }
   return hipGetLastError();
 }
 
 template <class E>
 hipError_t probs_from_lse(const float* s, const float* lse, void* p, long long n_rows, int T,
                           float scale_log2, int causal, hipStream_t st) {
-  if (T % 4 == 0)
-    probs_from_lse_kernel<E, 4><<<row_grid(n_rows), kThreads, 0, st>>>(
-        s, lse, static_cast<uint16_t*>(p), n_rows, T, scale_log2, causal);
-  else
-    probs_from_lse_kernel<E, 1><<<row_grid(n_rows), kThreads, 0, st>>>(
-        s, lse, static_cast<uint16_t*>(p), n_rows, T, scale_log2, causal);
+  uint16_t* p16 = static_cast<uint16_t*>(p);
+  if (resident_chunks(T) > 0) {
+    RCA_RESIDENT_DISPATCH(probs_from_lse_resident, s, lse, p16, n_rows, T, scale_log2, causal)
+  } else if (T % 4 == 0) {
+    probs_from_lse_kernel<E, 4><<<row_grid(n_rows), kThreads, 0, st>>>(s, lse, p16, n_rows, T,
+                                                                        scale_log2, causal);
+  } else {
+    probs_from_lse_kernel<E, 1><<<row_grid(n_rows), kThreads, 0, st>>>(s, lse, p16, n_rows, T,
+                                                                        scale_log2, causal);
+  }
   return hipGetLastError();
 }
 
 template <class E>
 hipError_t softmax_bwd(const void* p, const float* dp, void* ds, long long n_rows, int T,
                        int causal, hipStream_t st) {
-  if (T % 4 == 0)
-    softmax_bwd_kernel<E, 4><<<row_grid(n_rows), kThreads, 0, st>>>(
-        static_cast<const uint16_t*>(p), dp, static_cast<uint16_t*>(ds), n_rows, T, causal);
-  else
-    softmax_bwd_kernel<E, 1><<<row_grid(n_rows), kThreads, 0, st>>>(
-        static_cast<const uint16_t*>(p), dp, static_cast<uint16_t*>(ds), n_rows, T, causal);
-  return hipGetLastError();
-}
-
-template <class E>
-hipError_t convert(const float* x, void* y, long long n, hipStream_t st) {
-  const long long blocks = (n + 1023) / 1024;
-  convert_kernel<E><<<dim3((unsigned)blocks), 256, 0, st>>>(x, static_cast<uint16_t*>(y), n);
+  const uint16_t* p16 = static_cast<const uint16_t*>(p);
+  uint16_t* ds16 = static_cast<uint16_t*>(ds);
+  if (resident_chunks(T) > 0) {
+    RCA_RESIDENT_DISPATCH(softmax_bwd_resident, p16, dp, ds16, n_rows, T, causal)
+  } else if (T % 4 == 0) {
+    softmax_bwd_kernel<E, 4><<<row_grid(n_rows), kThreads, 0, st>>>(p16, dp, ds16, n_rows, T,
+                                                                     causal);
+  } else {
+    softmax_bwd_kernel<E, 1><<<row_grid(n_rows), kThreads, 0, st>>>(p16, dp, ds16, n_rows, T,
+                                                                     causal);
+  }
   return hipGetLastError();
 }
 
@@ -276,8 +409,6 @@ template hipError_t probs_from_lse<Bf16>(const float*, const float*, void*, long
 template hipError_t probs_from_lse<F16>(const float*, const float*, void*, long long, int, float, int, hipStream_t);
 template hipError_t softmax_bwd<Bf16>(const void*, const float*, void*, long long, int, int, hipStream_t);
 template hipError_t softmax_bwd<F16>(const void*, const float*, void*, long long, int, int, hipStream_t);
-template hipError_t convert<Bf16>(const float*, void*, long long, hipStream_t);
-template hipError_t convert<F16>(const float*, void*, long long, hipStream_t);
 
 }  // namespace unf
 }  // namespace rca

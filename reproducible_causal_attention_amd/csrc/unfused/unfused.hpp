@@ -17,8 +17,14 @@ hipError_t probs_from_lse(const float* s, const float* lse, void* p, long long n
 template <class E>
 hipError_t softmax_bwd(const void* p, const float* dp, void* ds, long long n_rows, int T,
                        int causal, hipStream_t st);
+// out[b][t][h][:] = in[b][t][h / G][:] for the Hq = Hkv*G query heads; D % 8 == 0.
+hipError_t repeat_kv(const void* in, void* out, int B, int T, int Hkv, int G, int D,
+                     hipStream_t st);
+
+// out[b][j][g][d] = sum over r < G, in order, of in[b][g*G + r][j][d]; D % 4 == 0.
 template <class E>
-hipError_t convert(const float* x, void* y, long long n, hipStream_t st);
+hipError_t group_sum(const float* in, void* out, int B, int T, int Hkv, int G, int D,
+                     hipStream_t st);
 
 }  // namespace unf
 }  // namespace rca

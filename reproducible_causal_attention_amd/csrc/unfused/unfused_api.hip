@@ -3,10 +3,11 @@
 //
 // Tensors are row-major; rocBLAS is column-major, so a row-major [m, n] matrix
 // with row stride ld is passed as the column-major n x m matrix with leading
-// dimension ld.  The query heads h = g*G + r of KV head g share K/V; for a fixed
-// r, the heads over g are evenly strided in q (G*D elements) and in the [T, T]
-// matrices (G*T*T), and the KV heads in k, v (D), so each GEMM is one
-// strided-batched call over g per (batch element, r).
+// dimension ld.  With grouped heads the KV head of query head h is h / G, not
+// evenly strided in h, so K and V are first repeated to the Hq query heads in
+// the workspace; then every GEMM is one strided-batched call over the Hq heads
+// of each batch element.  dK and dV are formed per query head in float32 and
+// summed over each KV group in a fixed order.
 #include <rocblas/rocblas.h>
 
 #include "../../../include/attn_unfused.h"
@@ -38,18 +39,20 @@ attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dty
 }
 
 struct Layout {
-  size_t s, p, ds, dk32, dv32, total;  // byte offsets into the workspace
+  size_t s, p, ds, dkh, dvh, krep, vrep, total;  // byte offsets into the workspace
 };
 
-Layout layout(int B, int T, int Hq, int Hkv, int D) {
-  const size_t n = (size_t)B * Hq * T * T, m = (size_t)B * T * Hkv * D;
+Layout layout(int B, int T, int Hq, int D) {
+  const size_t n = (size_t)B * Hq * T * T, m = (size_t)B * Hq * T * D;
   Layout l;
   l.s = 0;
   l.p = l.s + round256(4 * n);
   l.ds = l.p + round256(2 * n);
-  l.dk32 = l.ds + round256(2 * n);
-  l.dv32 = l.dk32 + round256(4 * m);
-  l.total = l.dv32 + round256(4 * m);
+  l.dkh = l.ds + round256(2 * n);
+  l.dvh = l.dkh + round256(4 * m);
+  l.krep = l.dvh + round256(4 * m);
+  l.vrep = l.krep + round256(2 * m);
+  l.total = l.vrep + round256(2 * m);
   return l;
 }
 
@@ -67,15 +70,17 @@ attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E
     if (st_ != ATTN_OK) return st_;   \
   } while (0)
 
-// One strided-batched GEMM, column-major: C = alpha op(A) op(B) + beta C, inputs
-// of type `ab`, output of type `c`, float32 accumulation.
+// One strided-batched GEMM over the Hq heads of a batch element, column-major:
+// C_h = alpha op(A_h) op(B_h) + beta C_h; inputs of type `ab`, output of type
+// `ct`, float32 accumulation.
 struct Gemm {
   rocblas_handle h;
   rocblas_datatype ab;
+  int batch;
   attn_status_t operator()(rocblas_operation ta, rocblas_operation tb, int m, int n, int k,
                            float alpha, const void* a, int lda, long long sa, const void* b,
                            int ldb, long long sb, float beta, void* c, rocblas_datatype ct,
-                           int ldc, long long sc, int batch) const {
+                           int ldc, long long sc) const {
     return from_blas(rocblas_gemm_strided_batched_ex(
         h, ta, tb, m, n, k, &alpha, a, ab, lda, sa, b, ab, ldb, sb, &beta, c, ct, ldc, sc, c, ct,
         ldc, sc, batch, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0));
@@ -85,26 +90,17 @@ struct Gemm {
 constexpr rocblas_operation N_ = rocblas_operation_none;
 constexpr rocblas_operation T_ = rocblas_operation_transpose;
 
-// Shapes shared by the GEMMs of one call.
+// Sizes of one call; element offsets of batch element b in each kind of buffer.
 struct Shape {
   int B, T, Hq, Hkv, D, G;
-  size_t qe, ke, tt;  // elements per batch element of q and k, per [T, T] matrix
+  long long qe, tt, he;  // per batch element of q-shaped tensors; per [T, T]; per head [T, D]
   Shape(int B_, int T_, int Hq_, int Hkv_, int D_)
       : B(B_), T(T_), Hq(Hq_), Hkv(Hkv_), D(D_), G(Hq_ / Hkv_),
-        qe((size_t)T_ * Hq_ * D_), ke((size_t)T_ * Hkv_ * D_), tt((size_t)T_ * T_) {}
+        qe((long long)T_ * Hq_ * D_), tt((long long)T_ * T_), he((long long)T_ * D_) {}
 };
 
-// S[b, h] = x_h y_g^T as float32 [T, T] for every head (x: [B,T,Hq,D], y: [B,T,Hkv,D]).
-attn_status_t scores(const Gemm& gemm, const Shape& z, const uint16_t* x, const uint16_t* y,
-                     float* s) {
-  for (int b = 0; b < z.B; ++b)
-    for (int r = 0; r < z.G; ++r)
-      ATTN_TRY(gemm(T_, N_, z.T, z.T, z.D, 1.f, y + b * z.ke, z.Hkv * z.D, z.D,
-                    x + b * z.qe + (size_t)r * z.D, z.Hq * z.D, (long long)z.G * z.D, 0.f,
-                    s + ((size_t)b * z.Hq + r) * z.tt, rocblas_datatype_f32_r, z.T,
-                    (long long)z.G * z.tt, z.Hkv));
-  return ATTN_OK;
-}
+inline const char* at(const void* base, long long elems, int es) { return static_cast<const char*>(base) + elems * es; }
+inline char* at(void* base, long long elems, int es) { return static_cast<char*>(base) + elems * es; }
 
 template <class E>
 struct Launch;
@@ -117,67 +113,92 @@ struct Launch<rca::F16> {
   static constexpr rocblas_datatype type = rocblas_datatype_f16_r;
 };
 
-template <class E>
-attn_status_t run_fwd(rocblas_handle h, const Shape& z, const uint16_t* q, const uint16_t* k,
-                      const uint16_t* v, uint16_t* o, float* lse, float scale, int causal,
-                      char* ws, hipStream_t st) {
-  const Gemm gemm{h, Launch<E>::type};
-  const Layout l = layout(z.B, z.T, z.Hq, z.Hkv, z.D);
-  float* s = reinterpret_cast<float*>(ws + l.s);
-  uint16_t* p = reinterpret_cast<uint16_t*>(ws + l.p);
-  ATTN_TRY(scores(gemm, z, q, k, s));
-  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  ATTN_TRY(from_hip(rca::unf::softmax_lse<E>(s, p, lse, (long long)z.B * z.Hq * z.T, z.T,
-                                             scale_log2, causal, st)));
-  // o_h = P_h v_g: column-major (D x T_i) = v^T (D x T_j) . P^T (T_j x T_i).
+// K and V of every query head: the repeated copies in the workspace, or k, v
+// themselves without grouping.
+struct KV {
+  const void* k;
+  const void* v;
+};
+
+KV repeat_kv(const Shape& z, const void* k, const void* v, char* ws, const Layout& l,
+             hipStream_t st, attn_status_t& status) {
+  status = ATTN_OK;
+  if (z.G == 1) return KV{k, v};
+  void* kr = ws + l.krep;
+  void* vr = ws + l.vrep;
+  status = from_hip(rca::unf::repeat_kv(k, kr, z.B, z.T, z.Hkv, z.G, z.D, st));
+  if (status == ATTN_OK) status = from_hip(rca::unf::repeat_kv(v, vr, z.B, z.T, z.Hkv, z.G, z.D, st));
+  return KV{kr, vr};
+}
+
+// S_h = x_h y_h^T as float32 [T, T] for every head (x, y: [B, T, Hq, D]):
+// column-major (T_j x T_i) = y (T_j x D) . x^T (D x T_i).
+attn_status_t scores(const Gemm& gemm, const Shape& z, const void* x, const void* y, float* s) {
   for (int b = 0; b < z.B; ++b)
-    for (int r = 0; r < z.G; ++r)
-      ATTN_TRY(gemm(N_, N_, z.D, z.T, z.T, 1.f, v + b * z.ke, z.Hkv * z.D, z.D,
-                    p + ((size_t)b * z.Hq + r) * z.tt, z.T, (long long)z.G * z.tt, 0.f,
-                    o + b * z.qe + (size_t)r * z.D, Launch<E>::type, z.Hq * z.D,
-                    (long long)z.G * z.D, z.Hkv));
+    ATTN_TRY(gemm(T_, N_, z.T, z.T, z.D, 1.f, at(y, b * z.qe, 2), z.Hq * z.D, z.D,
+                  at(x, b * z.qe, 2), z.Hq * z.D, z.D, 0.f, s + b * z.Hq * z.tt,
+                  rocblas_datatype_f32_r, z.T, z.tt));
   return ATTN_OK;
 }
 
 template <class E>
-attn_status_t run_bwd(rocblas_handle h, const Shape& z, const uint16_t* q, const uint16_t* k,
-                      const uint16_t* v, const float* lse, const uint16_t* dO, uint16_t* dq,
-                      uint16_t* dk, uint16_t* dv, float scale, int causal, char* ws,
+attn_status_t run_fwd(rocblas_handle h, const Shape& z, const void* q, const void* k,
+                      const void* v, void* o, float* lse, float scale, int causal, char* ws,
                       hipStream_t st) {
-  const Gemm gemm{h, Launch<E>::type};
-  const Layout l = layout(z.B, z.T, z.Hq, z.Hkv, z.D);
+  const Layout l = layout(z.B, z.T, z.Hq, z.D);
+  const Gemm gemm{h, Launch<E>::type, z.Hq};
+  float* s = reinterpret_cast<float*>(ws + l.s);
+  void* p = ws + l.p;
+  attn_status_t status;
+  const KV kv = repeat_kv(z, k, v, ws, l, st, status);
+  ATTN_TRY(status);
+  ATTN_TRY(scores(gemm, z, q, kv.k, s));
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  ATTN_TRY(from_hip(rca::unf::softmax_lse<E>(s, p, lse, (long long)z.B * z.Hq * z.T, z.T,
+                                             scale_log2, causal, st)));
+  // o_h = P_h v_h: column-major (D x T_i) = v^T (D x T_j) . P^T (T_j x T_i).
+  for (int b = 0; b < z.B; ++b)
+    ATTN_TRY(gemm(N_, N_, z.D, z.T, z.T, 1.f, at(kv.v, b * z.qe, 2), z.Hq * z.D, z.D,
+                  at(p, b * z.Hq * z.tt, 2), z.T, z.tt, 0.f, at(o, b * z.qe, 2), Launch<E>::type,
+                  z.Hq * z.D, z.D));
+  return ATTN_OK;
+}
+
+template <class E>
+attn_status_t run_bwd(rocblas_handle h, const Shape& z, const void* q, const void* k,
+                      const void* v, const float* lse, const void* dO, void* dq, void* dk,
+                      void* dv, float scale, int causal, char* ws, hipStream_t st) {
+  const Layout l = layout(z.B, z.T, z.Hq, z.D);
+  const Gemm gemm{h, Launch<E>::type, z.Hq};
   float* s = reinterpret_cast<float*>(ws + l.s);  // S, then dP
-  uint16_t* p = reinterpret_cast<uint16_t*>(ws + l.p);
-  uint16_t* ds = reinterpret_cast<uint16_t*>(ws + l.ds);
-  float* dk32 = reinterpret_cast<float*>(ws + l.dk32);
-  float* dv32 = reinterpret_cast<float*>(ws + l.dv32);
+  void* p = ws + l.p;
+  void* ds = ws + l.ds;
+  float* dkh = reinterpret_cast<float*>(ws + l.dkh);
+  float* dvh = reinterpret_cast<float*>(ws + l.dvh);
   const long long n_rows = (long long)z.B * z.Hq * z.T;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  ATTN_TRY(scores(gemm, z, q, k, s));
+  attn_status_t status;
+  const KV kv = repeat_kv(z, k, v, ws, l, st, status);
+  ATTN_TRY(status);
+  ATTN_TRY(scores(gemm, z, q, kv.k, s));
   ATTN_TRY(from_hip(rca::unf::probs_from_lse<E>(s, lse, p, n_rows, z.T, scale_log2, causal, st)));
-  ATTN_TRY(scores(gemm, z, dO, v, s));  // dP overwrites S (stream order)
+  ATTN_TRY(scores(gemm, z, dO, kv.v, s));  // dP overwrites S (stream order)
   ATTN_TRY(from_hip(rca::unf::softmax_bwd<E>(p, s, ds, n_rows, z.T, causal, st)));
   for (int b = 0; b < z.B; ++b) {
-    // dv_g = sum_r P_h^T dO_h and dk_g = scale sum_r dS_h^T q_h, heads r = 0..G-1 in
-    // order into float32: column-major (D x T_j) = x^T (D x T_i) . M (T_i x T_j).
-    for (int r = 0; r < z.G; ++r) {
-      const float beta = r == 0 ? 0.f : 1.f;
-      const size_t mo = ((size_t)b * z.Hq + r) * z.tt;
-      ATTN_TRY(gemm(N_, T_, z.D, z.T, z.T, 1.f, dO + b * z.qe + (size_t)r * z.D, z.Hq * z.D,
-                    (long long)z.G * z.D, p + mo, z.T, (long long)z.G * z.tt, beta,
-                    dv32 + b * z.ke, rocblas_datatype_f32_r, z.Hkv * z.D, z.D, z.Hkv));
-      ATTN_TRY(gemm(N_, T_, z.D, z.T, z.T, scale, q + b * z.qe + (size_t)r * z.D, z.Hq * z.D,
-                    (long long)z.G * z.D, ds + mo, z.T, (long long)z.G * z.tt, beta,
-                    dk32 + b * z.ke, rocblas_datatype_f32_r, z.Hkv * z.D, z.D, z.Hkv));
-      // dq_h = scale dS_h k_g: column-major (D x T_i) = k^T (D x T_j) . dS^T (T_j x T_i).
-      ATTN_TRY(gemm(N_, N_, z.D, z.T, z.T, scale, k + b * z.ke, z.Hkv * z.D, z.D, ds + mo, z.T,
-                    (long long)z.G * z.tt, 0.f, dq + b * z.qe + (size_t)r * z.D, Launch<E>::type,
-                    z.Hq * z.D, (long long)z.G * z.D, z.Hkv));
-    }
+    const long long mo = b * z.Hq * z.tt, ho = b * z.Hq * z.he;
+    // Per query head, float32 [T, D]: dv_h = P_h^T dO_h and dk_h = scale dS_h^T q_h,
+    // column-major (D x T_j) = x^T (D x T_i) . M (T_i x T_j).
+    ATTN_TRY(gemm(N_, T_, z.D, z.T, z.T, 1.f, at(dO, b * z.qe, 2), z.Hq * z.D, z.D,
+                  at(p, mo, 2), z.T, z.tt, 0.f, dvh + ho, rocblas_datatype_f32_r, z.D, z.he));
+    ATTN_TRY(gemm(N_, T_, z.D, z.T, z.T, scale, at(q, b * z.qe, 2), z.Hq * z.D, z.D,
+                  at(ds, mo, 2), z.T, z.tt, 0.f, dkh + ho, rocblas_datatype_f32_r, z.D, z.he));
+    // dq_h = scale dS_h k_h: column-major (D x T_i) = k^T (D x T_j) . dS^T (T_j x T_i).
+    ATTN_TRY(gemm(N_, N_, z.D, z.T, z.T, scale, at(kv.k, b * z.qe, 2), z.Hq * z.D, z.D,
+                  at(ds, mo, 2), z.T, z.tt, 0.f, at(dq, b * z.qe, 2), Launch<E>::type,
+                  z.Hq * z.D, z.D));
   }
-  const long long m = (long long)z.B * z.ke;
-  ATTN_TRY(from_hip(rca::unf::convert<E>(dk32, dk, m, st)));
-  return from_hip(rca::unf::convert<E>(dv32, dv, m, st));
+  ATTN_TRY(from_hip(rca::unf::group_sum<E>(dkh, dk, z.B, z.T, z.Hkv, z.G, z.D, st)));
+  return from_hip(rca::unf::group_sum<E>(dvh, dv, z.B, z.T, z.Hkv, z.G, z.D, st));
 }
 
 attn_status_t bind(attn_unfused_ctx* ctx, void* stream) {
@@ -211,7 +232,7 @@ ATTN_EXPORT void attn_unfused_destroy(attn_unfused_ctx* ctx) {
 ATTN_EXPORT size_t attn_unfused_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
                                                 attn_dtype_t dtype) {
   if (check_shape(B, T, Hq, Hkv, D, dtype) != ATTN_OK) return 0;
-  return layout(B, T, Hq, Hkv, D).total;
+  return layout(B, T, Hq, D).total;
 }
 
 ATTN_EXPORT attn_status_t attn_unfused_fwd(attn_unfused_ctx* ctx, const void* q, const void* k,
@@ -223,7 +244,7 @@ ATTN_EXPORT attn_status_t attn_unfused_fwd(attn_unfused_ctx* ctx, const void* q,
   ATTN_TRY(check_ptrs({q, k, v, o, lse, workspace}));
   ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
   ATTN_TRY(check_scalars(scale, causal));
-  const size_t need = layout(B, T, Hq, Hkv, D).total;
+  const size_t need = layout(B, T, Hq, D).total;
   if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
   const size_t qb = (size_t)B * T * Hq * D * 2, kb = (size_t)B * T * Hkv * D * 2;
   const size_t lb = (size_t)B * Hq * T * sizeof(float);
@@ -232,13 +253,10 @@ ATTN_EXPORT attn_status_t attn_unfused_fwd(attn_unfused_ctx* ctx, const void* q,
   ATTN_TRY(bind(ctx, stream));
   const Shape z(B, T, Hq, Hkv, D);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  auto q16 = static_cast<const uint16_t*>(q), k16 = static_cast<const uint16_t*>(k),
-       v16 = static_cast<const uint16_t*>(v);
-  auto o16 = static_cast<uint16_t*>(o);
   char* ws = static_cast<char*>(workspace);
   return dtype == ATTN_BF16
-             ? run_fwd<rca::Bf16>(ctx->blas, z, q16, k16, v16, o16, lse, scale, causal, ws, st)
-             : run_fwd<rca::F16>(ctx->blas, z, q16, k16, v16, o16, lse, scale, causal, ws, st);
+             ? run_fwd<rca::Bf16>(ctx->blas, z, q, k, v, o, lse, scale, causal, ws, st)
+             : run_fwd<rca::F16>(ctx->blas, z, q, k, v, o, lse, scale, causal, ws, st);
 }
 
 ATTN_EXPORT attn_status_t attn_unfused_bwd(attn_unfused_ctx* ctx, const void* q, const void* k,
@@ -251,7 +269,7 @@ ATTN_EXPORT attn_status_t attn_unfused_bwd(attn_unfused_ctx* ctx, const void* q,
   ATTN_TRY(check_ptrs({q, k, v, lse, dO, dq, dk, dv, workspace}));
   ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
   ATTN_TRY(check_scalars(scale, causal));
-  const size_t need = layout(B, T, Hq, Hkv, D).total;
+  const size_t need = layout(B, T, Hq, D).total;
   if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
   const size_t qb = (size_t)B * T * Hq * D * 2, kb = (size_t)B * T * Hkv * D * 2;
   const size_t lb = (size_t)B * Hq * T * sizeof(float);
@@ -262,14 +280,10 @@ ATTN_EXPORT attn_status_t attn_unfused_bwd(attn_unfused_ctx* ctx, const void* q,
   ATTN_TRY(bind(ctx, stream));
   const Shape z(B, T, Hq, Hkv, D);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  auto c16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
-  auto m16 = [](void* x) { return static_cast<uint16_t*>(x); };
   char* ws = static_cast<char*>(workspace);
   return dtype == ATTN_BF16
-             ? run_bwd<rca::Bf16>(ctx->blas, z, c16(q), c16(k), c16(v), lse, c16(dO), m16(dq),
-                                  m16(dk), m16(dv), scale, causal, ws, st)
-             : run_bwd<rca::F16>(ctx->blas, z, c16(q), c16(k), c16(v), lse, c16(dO), m16(dq),
-                                 m16(dk), m16(dv), scale, causal, ws, st);
+             ? run_bwd<rca::Bf16>(ctx->blas, z, q, k, v, lse, dO, dq, dk, dv, scale, causal, ws, st)
+             : run_bwd<rca::F16>(ctx->blas, z, q, k, v, lse, dO, dq, dk, dv, scale, causal, ws, st);
 }
 
 namespace {

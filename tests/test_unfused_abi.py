@@ -39,10 +39,11 @@ def test_library_exports_every_declared_function(lib):
 def test_workspace_bytes(lib):
     f = lib.attn_unfused_workspace_bytes
     n = 4 * 12 * 1024 * 1024
-    m = 4 * 1024 * 4 * 64
-    assert f(4, 1024, 12, 4, 64, A.ATTN_BF16) == 4 * n + 2 * n + 2 * n + 4 * m + 4 * m
-    # S 392 -> 512, P and dS 196 -> 256 each, dk/dv accumulators 1792 each
-    assert f(1, 7, 2, 1, 64, A.ATTN_F16) == 512 + 256 + 256 + 1792 + 1792
+    m = 4 * 12 * 1024 * 64
+    # S, P, dS; per-head dk, dv partials (float32); k, v repeated to 12 heads (16-bit)
+    assert f(4, 1024, 12, 4, 64, A.ATTN_BF16) == 4 * n + 2 * n + 2 * n + 4 * m + 4 * m + 2 * m + 2 * m
+    # S 392 -> 512, P and dS 196 -> 256 each, partials 3584 each, repeated k, v 1792 each
+    assert f(1, 7, 2, 1, 64, A.ATTN_F16) == 512 + 256 + 256 + 3584 + 3584 + 1792 + 1792
     assert f(1, 7, 2, 1, 64, A.ATTN_F32) == 0   # 16-bit only
     assert f(1, 7, 3, 2, 64, A.ATTN_BF16) == 0  # Hq not a multiple of Hkv
     assert f(1, 7, 2, 1, 60, A.ATTN_BF16) == 0  # D not a multiple of 8
