@@ -23,6 +23,9 @@
  *   dq[i] = scale * sum_j dS[i][j] k[j];  dk[j] = scale * sum_{h in group} sum_i dS[i][j] q[i];
  *   dv[j] = sum_{h in group} sum_i P[i][j] dO[i].
  *
+ * Head dimension D: 64 for every dtype; 128 for ATTN_BF16 and ATTN_F16 (the same
+ * kernels instantiated for 128-wide rows).
+ *
  * Layouts (all row-major and contiguous; there are no stride arguments):
  *   q, o, dO, dq : [B, T, Hq,  D] elements of the input dtype
  *   k, v, dk, dv : [B, T, Hkv, D] elements of the input dtype
@@ -49,8 +52,10 @@
  * pointer not 16-byte aligned; an output range overlapping an input range or
  * another output; a workspace smaller than attn_bwd_workspace_bytes() (or
  * attn_bwd_rope_workspace_bytes() for attn_bwd_rope); sizes
- * beyond the limits below.  ATTN_ERR_UNSUPPORTED: D != 64, an unknown dtype, or
- * ATTN_F32 in a rotary entry point.
+ * beyond the limits below.  ATTN_ERR_UNSUPPORTED: D other than 64 (or 128 with
+ * ATTN_BF16 / ATTN_F16), an unknown dtype, or ATTN_F32 in a rotary entry point;
+ * it is reported only for calls whose other arguments pass the checks above
+ * (the overlap rule included).
  * ATTN_ERR_HIP: the HIP runtime reported an error for a launch (the value of
  * hipGetLastError() after the launch; an error pending from an earlier,
  * unrelated runtime call is discarded before the launch, so it is not reported

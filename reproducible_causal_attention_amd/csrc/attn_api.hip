@@ -25,8 +25,14 @@ constexpr long long kMaxTiles = 1LL << 23;     // ceil(T/64) * B * Hq
 constexpr long long kMaxElements = 1LL << 40;  // per tensor
 constexpr long long kMaxBatchBytes = 1LL << 31; // one batch element of any tensor (buffer offsets are 32-bit)
 
-// Sizes and dtype, shared by every entry point (Hkv = Hq where no KV tensor is involved).
-attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype) {
+#define ATTN_TRY(expr)                       \
+  do {                                       \
+    const attn_status_t st_ = (expr);        \
+    if (st_ != ATTN_OK) return st_;          \
+  } while (0)
+
+// Sizes, shared by every entry point (Hkv = Hq where no KV tensor is involved).
+attn_status_t check_sizes(int B, int T, int Hq, int Hkv, int D) {
   if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (T > kMaxT) return ATTN_ERR_INVALID_ARG;
@@ -34,13 +40,25 @@ attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dty
   if (tiles >= kMaxTiles) return ATTN_ERR_INVALID_ARG;
   if ((long long)B * T * Hq * (long long)D >= kMaxElements) return ATTN_ERR_INVALID_ARG;
   if ((long long)T * Hq * (long long)D * 4 >= kMaxBatchBytes) return ATTN_ERR_INVALID_ARG;
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
-  if (D != rca::kHeadDim) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
-rca::Problem make_problem(int B, int T, int Hq, int Hkv, float scale, int causal) {
+// What the kernels implement: head dim 64 for every dtype, 128 for the 16-bit ones.
+// Checked after the argument checks, so an invalid call is reported as such.
+attn_status_t check_supported(int D, attn_dtype_t dtype) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+  if (D != rca::kHeadDim && !(D == 128 && dtype != ATTN_F32)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status_t check_shape(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype) {
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
+  return check_supported(D, dtype);
+}
+
+rca::Problem make_problem(int B, int T, int Hq, int Hkv, float scale, int causal, int D) {
   rca::Problem p;
+  p.D = D;
   p.B = B;
   p.T = T;
   p.Hq = Hq;
@@ -64,11 +82,6 @@ attn_status_t check_rope_dtype(attn_dtype_t dtype) {
   return dtype == ATTN_BF16 || dtype == ATTN_F16 ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
 }
 
-#define ATTN_TRY(expr)                       \
-  do {                                       \
-    const attn_status_t st_ = (expr);        \
-    if (st_ != ATTN_OK) return st_;          \
-  } while (0)
 
 }  // namespace
 
@@ -76,15 +89,16 @@ ATTN_EXPORT attn_status_t attn_fwd(const void* q, const void* k, const void* v, 
                                    int B, int T, int Hq, int Hkv, int D, float scale, int causal,
                                    attn_dtype_t dtype, void* stream) {
   ATTN_TRY(check_ptrs({q, k, v, o, lse}));
-  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
   ATTN_TRY(check_scalars(scale, causal));
   const size_t es = elem_size(dtype);
   const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
   const size_t lb = (size_t)B * Hq * T * sizeof(float);
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb)},
                           {span_of(o, qb), span_of(lse, lb)}));
+  ATTN_TRY(check_supported(D, dtype));
   discard_stale_error();
-  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16  ? rca::launch_fwd_bf16(p, q, k, v, o, lse, s)
                   : dtype == ATTN_F16 ? rca::launch_fwd_f16(p, q, k, v, o, lse, s)
@@ -100,12 +114,13 @@ ATTN_EXPORT attn_status_t attn_bwd_preprocess(const void* o, const void* dO, flo
                                               int T, int Hq, int D, attn_dtype_t dtype,
                                               void* stream) {
   ATTN_TRY(check_ptrs({o, dO, delta}));
-  ATTN_TRY(check_shape(B, T, Hq, Hq, D, dtype));
+  ATTN_TRY(check_sizes(B, T, Hq, Hq, D));
   const size_t qb = (size_t)B * T * Hq * D * elem_size(dtype);
   const size_t lb = (size_t)B * Hq * T * sizeof(float);
   ATTN_TRY(check_disjoint({span_of(o, qb), span_of(dO, qb)}, {span_of(delta, lb)}));
+  ATTN_TRY(check_supported(D, dtype));
   discard_stale_error();
-  const rca::Problem p = make_problem(B, T, Hq, Hq, 1.0f, 1);
+  const rca::Problem p = make_problem(B, T, Hq, Hq, 1.0f, 1, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16  ? rca::launch_bwd_pre_bf16(p, o, dO, delta, s)
                   : dtype == ATTN_F16 ? rca::launch_bwd_pre_f16(p, o, dO, delta, s)
@@ -117,7 +132,7 @@ ATTN_EXPORT attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void
                                         int B, int T, int Hq, int Hkv, int D, float scale,
                                         int causal, attn_dtype_t dtype, void* stream) {
   ATTN_TRY(check_ptrs({q, k, v, dO, lse, delta, dk, dv}));
-  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
   ATTN_TRY(check_scalars(scale, causal));
   const size_t es = elem_size(dtype);
   const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
@@ -125,8 +140,9 @@ ATTN_EXPORT attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(dO, qb),
                            span_of(lse, lb), span_of(delta, lb)},
                           {span_of(dk, kb), span_of(dv, kb)}));
+  ATTN_TRY(check_supported(D, dtype));
   discard_stale_error();
-  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16  ? rca::launch_bwd_dkdv_bf16(p, q, k, v, dO, lse, delta, dk, dv, s)
                   : dtype == ATTN_F16 ? rca::launch_bwd_dkdv_f16(p, q, k, v, dO, lse, delta, dk, dv, s)
@@ -138,7 +154,7 @@ ATTN_EXPORT attn_status_t attn_bwd_dq(const void* q, const void* k, const void* 
                                       int Hq, int Hkv, int D, float scale, int causal,
                                       attn_dtype_t dtype, void* stream) {
   ATTN_TRY(check_ptrs({q, k, v, dO, lse, delta, dq}));
-  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
   ATTN_TRY(check_scalars(scale, causal));
   const size_t es = elem_size(dtype);
   const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
@@ -146,8 +162,9 @@ ATTN_EXPORT attn_status_t attn_bwd_dq(const void* q, const void* k, const void* 
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(dO, qb),
                            span_of(lse, lb), span_of(delta, lb)},
                           {span_of(dq, qb)}));
+  ATTN_TRY(check_supported(D, dtype));
   discard_stale_error();
-  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16  ? rca::launch_bwd_dq_bf16(p, q, k, v, dO, lse, delta, dq, s)
                   : dtype == ATTN_F16 ? rca::launch_bwd_dq_f16(p, q, k, v, dO, lse, delta, dq, s)
@@ -160,7 +177,7 @@ ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, 
                                    attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   ATTN_TRY(check_ptrs({q, k, v, o, lse, dO, dq, dk, dv, workspace}));
-  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
   ATTN_TRY(check_scalars(scale, causal));
   const size_t need = attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype);
   if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
@@ -172,8 +189,9 @@ ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, 
                           {span_of(dq, qb), span_of(dk, kb), span_of(dv, kb),
                            span_of(workspace, need)}));
   float* delta = static_cast<float*>(workspace);
+  ATTN_TRY(check_supported(D, dtype));
   discard_stale_error();
-  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16) {
     ATTN_TRY(from_hip(rca::launch_bwd_pre_bf16(p, o, dO, delta, s)));
@@ -194,7 +212,7 @@ ATTN_EXPORT attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const v
                                            int Hkv, int D, float scale, int causal,
                                            attn_dtype_t dtype, void* stream) {
   ATTN_TRY(check_ptrs({q, k, v, dO, lse, delta, dq, dk, dv}));
-  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
   ATTN_TRY(check_scalars(scale, causal));
   const size_t es = elem_size(dtype);
   const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
@@ -202,8 +220,9 @@ ATTN_EXPORT attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const v
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(dO, qb),
                            span_of(lse, lb), span_of(delta, lb)},
                           {span_of(dq, qb), span_of(dk, kb), span_of(dv, kb)}));
+  ATTN_TRY(check_supported(D, dtype));
   discard_stale_error();
-  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16)
     return from_hip(rca::launch_bwd_dkdv_dq_bf16(p, q, k, v, dO, lse, delta, dq, dk, dv, s));
@@ -218,16 +237,17 @@ ATTN_EXPORT attn_status_t attn_fwd_rope(const void* q, const void* k, const void
                                         float* lse, int B, int T, int Hq, int Hkv, int D,
                                         float scale, int causal, attn_dtype_t dtype, void* stream) {
   ATTN_TRY(check_ptrs({q, k, v, rope_cos, rope_sin, o, lse}));
-  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
   ATTN_TRY(check_scalars(scale, causal));
-  ATTN_TRY(check_rope_dtype(dtype));
   const size_t qb = (size_t)B * T * Hq * D * 2, kb = (size_t)B * T * Hkv * D * 2;
   const size_t lb = (size_t)B * Hq * T * sizeof(float), tb = (size_t)T * (D / 2) * sizeof(float);
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(rope_cos, tb),
                            span_of(rope_sin, tb)},
                           {span_of(o, qb), span_of(lse, lb)}));
+  ATTN_TRY(check_supported(D, dtype));
+  ATTN_TRY(check_rope_dtype(dtype));
   discard_stale_error();
-  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(dtype == ATTN_BF16
                       ? rca::launch_fwd_rope_bf16(p, q, k, v, rope_cos, rope_sin, o, lse, s)
@@ -249,9 +269,8 @@ ATTN_EXPORT attn_status_t attn_bwd_rope(const void* q, const void* k, const void
                                         attn_dtype_t dtype, void* workspace,
                                         size_t workspace_bytes, void* stream) {
   ATTN_TRY(check_ptrs({q, k, v, o, lse, dO, rope_cos, rope_sin, dq, dk, dv, workspace}));
-  ATTN_TRY(check_shape(B, T, Hq, Hkv, D, dtype));
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
   ATTN_TRY(check_scalars(scale, causal));
-  ATTN_TRY(check_rope_dtype(dtype));
   const size_t need = attn_bwd_rope_workspace_bytes(B, T, Hq, Hkv, D, dtype);
   if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
   const size_t qb = (size_t)B * T * Hq * D * 2, kb = (size_t)B * T * Hkv * D * 2;
@@ -265,8 +284,10 @@ ATTN_EXPORT attn_status_t attn_bwd_rope(const void* q, const void* k, const void
   float* delta = reinterpret_cast<float*>(ws);
   void* q_rot = ws + round256(lb);
   void* k_rot = ws + round256(lb) + round256(qb);
+  ATTN_TRY(check_supported(D, dtype));
+  ATTN_TRY(check_rope_dtype(dtype));
   discard_stale_error();
-  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal);
+  const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16) {
     ATTN_TRY(from_hip(rca::launch_bwd_rope_prep_bf16(p, o, dO, q, k, rope_cos, rope_sin, delta,

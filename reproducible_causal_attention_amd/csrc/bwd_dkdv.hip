@@ -5,14 +5,14 @@
 namespace rca {
 namespace {
 
-template <class E>
+template <class E, int kD>
 __global__ __launch_bounds__(dkdv::NTHREADS) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
     float scale, float scale_log2, int causal) {
-  __shared__ __attribute__((aligned(16))) char smem[dkdv::SMEM_BYTES];
-  dkdv::unit_body<E, false>(smem, blockIdx.x, q, k, v, dO, lse, delta, nullptr, nullptr, dk, dv, B,
+  __shared__ __attribute__((aligned(16))) char smem[dkdv::Dims<kD>::SMEM_BYTES];
+  dkdv::unit_body<E, false, kD>(smem, blockIdx.x, q, k, v, dO, lse, delta, nullptr, nullptr, dk, dv, B,
                             T, Hq, Hkv, scale, scale_log2, causal);
 }
 
@@ -25,7 +25,8 @@ hipError_t launch_bwd_dkdv_e(const Problem& p, const void* q, const void* k, con
   const int nkb = (p.T + 31) / 32;
   const int npairs = (nkb + 1) / 2;
   const dim3 grid((unsigned)(npairs * p.B * p.Hkv));
-  attn_bwd_dkdv_kernel<E><<<grid, dkdv::NTHREADS, 0, s>>>(
+  auto kernel = p.D == 128 ? attn_bwd_dkdv_kernel<E, 128> : attn_bwd_dkdv_kernel<E, 64>;
+  kernel<<<grid, dkdv::NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta,
       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), p.B, p.T, p.Hq, p.Hkv, p.scale,
@@ -46,7 +47,7 @@ hipError_t launch_bwd_dkdv_f16(const Problem& p, const void* q, const void* k, c
 }
 
 const char* bwd_dkdv_tiles() {
-  return "dkdv_bf16{key_block=32,waves=8,pairs=(j,n-1-j),query_step=32,mfma=32x32x16,lds_dma_x2}";
+  return "dkdv_bf16{key_block=32,waves=8,pairs=(j,n-1-j),query_step=32,mfma=32x32x16,lds_dma_x2,D=64|128(x1)}";
 }
 
 }  // namespace rca

@@ -16,26 +16,30 @@ namespace {
 
 constexpr int kThreads = dkdv::NTHREADS;
 static_assert(dqb::NTHREADS == kThreads, "both bodies run 512-thread workgroups");
-constexpr int kSmemBytes = dkdv::SMEM_BYTES > dqb::SMEM_BYTES ? dkdv::SMEM_BYTES : dqb::SMEM_BYTES;
+template <int kD>
+constexpr int smem_bytes() {
+  return dkdv::Dims<kD>::SMEM_BYTES > dqb::Dims<kD>::SMEM_BYTES ? dkdv::Dims<kD>::SMEM_BYTES
+                                                                : dqb::Dims<kD>::SMEM_BYTES;
+}
 
 // Workgroup i < n_dq runs dQ unit i; n_dq <= i < kv_base exit at once (padding,
 // so that dK/dV unit u keeps the XCD, i % 8, it has in its own grid); then dK/dV
 // unit i - kv_base.  kRope: q and k are the rotated q', k' and dq, dk are mapped
 // back through the rotations in the epilogues (tables rcos, rsin).
-template <class E, bool kRope>
+template <class E, bool kRope, int kD>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dq,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
     float scale, float scale_log2, int causal, int n_dq, int kv_base) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<kD>()];
   const int i = blockIdx.x;
   if (i < n_dq) {
-    dqb::unit_body<E, kRope>(smem, i, q, k, v, dO, lse, delta, rcos, rsin, dq, B, T, Hq, Hkv,
+    dqb::unit_body<E, kRope, kD>(smem, i, q, k, v, dO, lse, delta, rcos, rsin, dq, B, T, Hq, Hkv,
                              scale, scale_log2, causal);
   } else if (i >= kv_base) {
-    dkdv::unit_body<E, kRope>(smem, i - kv_base, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T,
+    dkdv::unit_body<E, kRope, kD>(smem, i - kv_base, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T,
                               Hq, Hkv, scale, scale_log2, causal);
   }
 }
@@ -52,7 +56,8 @@ hipError_t launch_bwd_dkdv_dq_e(const Problem& p, const void* q, const void* k, 
   const int nkb = (p.T + 31) / 32;
   const int n_kv = (nkb + 1) / 2 * p.B * p.Hkv;
   const dim3 grid((unsigned)(kv_base + n_kv));
-  attn_bwd_dkdv_dq_kernel<E, kRope><<<grid, kThreads, 0, s>>>(
+  auto kernel = p.D == 128 ? attn_bwd_dkdv_dq_kernel<E, kRope, 128> : attn_bwd_dkdv_dq_kernel<E, kRope, 64>;
+  kernel<<<grid, kThreads, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta, rcos, rsin,
       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), p.B,

@@ -5,14 +5,14 @@
 namespace rca {
 namespace {
 
-template <class E>
+template <class E, int kD>
 __global__ __launch_bounds__(dqb::NTHREADS) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dq, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
     int causal) {
-  __shared__ __attribute__((aligned(16))) char smem[dqb::SMEM_BYTES];
-  dqb::unit_body<E, false>(smem, blockIdx.x, q, k, v, dO, lse, delta, nullptr, nullptr, dq, B, T,
+  __shared__ __attribute__((aligned(16))) char smem[dqb::Dims<kD>::SMEM_BYTES];
+  dqb::unit_body<E, false, kD>(smem, blockIdx.x, q, k, v, dO, lse, delta, nullptr, nullptr, dq, B, T,
                            Hq, Hkv, scale, scale_log2, causal);
 }
 
@@ -24,7 +24,8 @@ hipError_t launch_bwd_dq_e(const Problem& p, const void* q, const void* k, const
                               hipStream_t s) {
   const int n_qt = (p.T + dqb::BM - 1) / dqb::BM;
   const dim3 grid((unsigned)(n_qt * p.B * p.Hq));
-  attn_bwd_dq_kernel<E><<<grid, dqb::NTHREADS, 0, s>>>(
+  auto kernel = p.D == 128 ? attn_bwd_dq_kernel<E, 128> : attn_bwd_dq_kernel<E, 64>;
+  kernel<<<grid, dqb::NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta,
       static_cast<uint16_t*>(dq), p.B, p.T, p.Hq, p.Hkv, p.scale, p.scale_log2, p.causal);
@@ -43,6 +44,6 @@ hipError_t launch_bwd_dq_f16(const Problem& p, const void* q, const void* k, con
   return launch_bwd_dq_e<F16>(p, q, k, v, dO, lse, delta, dq, s);
 }
 
-const char* bwd_dq_tiles() { return "dq_bf16{BM=128,BN=64,waves=8(4 query x 2 key),mfma=32x32x16}"; }
+const char* bwd_dq_tiles() { return "dq_bf16{BM=128,BN=64,waves=8(4 query x 2 key),mfma=32x32x16,D=64|128}"; }
 
 }  // namespace rca

@@ -5,9 +5,9 @@
 // unfused causal_softmax_bwd kernel of "Training a 100M transformer in pure
 // Rust: RustingBrain vs PyTorch and TensorFlow" (section "Step 1: measure before
 // changing anything") needs.  It reads o and dO once and writes one float per
-// row: HBM-bound.  Eight lanes share one 64-wide row (16 bytes each, whole rows
-// per wave instruction) and combine their partial dot products with a fixed
-// butterfly, so the result is reproducible.
+// row: HBM-bound.  Eight lanes share one row (16 bytes each per 64 columns,
+// whole rows per wave instruction) and combine their partial dot products with
+// a fixed butterfly, so the result is reproducible.
 #include "cdna4.hpp"
 #include "launch.hpp"
 
@@ -15,9 +15,11 @@ namespace rca {
 namespace {
 
 constexpr int PRE_THREADS = 256;
-constexpr int PRE_ROWS = PRE_THREADS / 8;  // 8 lanes x 8 elements per 64-wide row
+constexpr int PRE_ROWS = PRE_THREADS / 8;  // 8 lanes per row, 8 elements each per 64 columns
 
-template <class E>
+// Row of kD elements: lane `part` of the row's eight holds columns
+// 8*part + 64c + 0..7 for c < kD/64.
+template <class E, int kD>
 __device__ __forceinline__ void delta_rows(int blk, const uint16_t* __restrict__ o,
                                            const uint16_t* __restrict__ dO,
                                            float* __restrict__ delta, int T, int Hq,
@@ -26,12 +28,19 @@ __device__ __forceinline__ void delta_rows(int blk, const uint16_t* __restrict__
   const int part = threadIdx.x & 7;
   float acc = 0.f;
   if (row < n_rows) {
-    const u32x4_t a = gload16(o + row * kHeadDim + part * 8);
-    const u32x4_t c = gload16(dO + row * kHeadDim + part * 8);
+    u32x4_t a[kD / 64], c[kD / 64];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(E::lo(a[i]), E::lo(c[i]), acc);
-      acc = fmaf(E::hi(a[i]), E::hi(c[i]), acc);
+    for (int ch = 0; ch < kD / 64; ++ch) {
+      a[ch] = gload16(o + row * kD + part * 8 + 64 * ch);
+      c[ch] = gload16(dO + row * kD + part * 8 + 64 * ch);
+    }
+#pragma unroll
+    for (int ch = 0; ch < kD / 64; ++ch) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(E::lo(a[ch][i]), E::lo(c[ch][i]), acc);
+        acc = fmaf(E::hi(a[ch][i]), E::hi(c[ch][i]), acc);
+      }
     }
   }
   // Fixed butterfly over the 8 lanes of the row.
@@ -48,18 +57,18 @@ __device__ __forceinline__ void delta_rows(int blk, const uint16_t* __restrict__
   }
 }
 
-template <class E>
+template <class E, int kD>
 __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO, float* __restrict__ delta,
     int T, int Hq, long long n_rows) {
-  delta_rows<E>(blockIdx.x, o, dO, delta, T, Hq, n_rows);
+  delta_rows<E, kD>(blockIdx.x, o, dO, delta, T, Hq, n_rows);
 }
 
 // Backward preparation with rotary embedding: blocks [0, nb) write delta exactly
 // as attn_bwd_pre_kernel does, blocks [nb, 2nb) the rotated q rows and the rest
 // the rotated k rows (rope_rotate, as the forward rotates them as it loads:
 // the same bits), which the dK/dV and dQ kernels then read in place of q, k.
-template <class E>
+template <class E, int kD>
 __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_rope_prep_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -68,7 +77,7 @@ __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_rope_prep_kernel(
     long long n_qrows, long long n_krows, int nb) {
   int blk = blockIdx.x;
   if (blk < nb) {
-    delta_rows<E>(blk, o, dO, delta, T, Hq, n_qrows);
+    delta_rows<E, kD>(blk, o, dO, delta, T, Hq, n_qrows);
     return;
   }
   blk -= nb;
@@ -84,17 +93,21 @@ __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_rope_prep_kernel(
     n_rows = n_krows;
   }
   const long long row = (long long)blk * PRE_ROWS + (threadIdx.x >> 3);  // [b][t][h]
-  const int part = threadIdx.x & 7;  // elements 8*part .. +7, pairs 4*part .. +3
+  const int part = threadIdx.x & 7;  // elements 8*part + 64ch .. +7, pairs 4*part + 32ch .. +3
   if (row < n_rows) {
     const int t = (int)((row / H) % T);
-    u32x4_t x = gload16(src + row * kHeadDim + part * 8);
-    const float4 c = *reinterpret_cast<const float4*>(rcos + (size_t)t * 32 + part * 4);
-    const float4 s = *reinterpret_cast<const float4*>(rsin + (size_t)t * 32 + part * 4);
-    x[0] = rope_rotate<E>(x[0], c.x, s.x);
-    x[1] = rope_rotate<E>(x[1], c.y, s.y);
-    x[2] = rope_rotate<E>(x[2], c.z, s.z);
-    x[3] = rope_rotate<E>(x[3], c.w, s.w);
-    *reinterpret_cast<u32x4_t*>(dst + row * kHeadDim + part * 8) = x;
+#pragma unroll
+    for (int ch = 0; ch < kD / 64; ++ch) {
+      u32x4_t x = gload16(src + row * kD + part * 8 + 64 * ch);
+      const size_t ti = (size_t)t * (kD / 2) + part * 4 + 32 * ch;
+      const float4 c = *reinterpret_cast<const float4*>(rcos + ti);
+      const float4 s = *reinterpret_cast<const float4*>(rsin + ti);
+      x[0] = rope_rotate<E>(x[0], c.x, s.x);
+      x[1] = rope_rotate<E>(x[1], c.y, s.y);
+      x[2] = rope_rotate<E>(x[2], c.z, s.z);
+      x[3] = rope_rotate<E>(x[3], c.w, s.w);
+      *reinterpret_cast<u32x4_t*>(dst + row * kD + part * 8 + 64 * ch) = x;
+    }
   }
 }
 
@@ -105,8 +118,9 @@ hipError_t launch_bwd_pre_e(const Problem& p, const void* o, const void* dO, flo
                                hipStream_t s) {
   const long long n_rows = (long long)p.B * p.T * p.Hq;
   const dim3 grid((unsigned)((n_rows + PRE_ROWS - 1) / PRE_ROWS));
-  attn_bwd_pre_kernel<E><<<grid, PRE_THREADS, 0, s>>>(
-      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), delta, p.T, p.Hq, n_rows);
+  auto kernel = p.D == 128 ? attn_bwd_pre_kernel<E, 128> : attn_bwd_pre_kernel<E, 64>;
+  kernel<<<grid, PRE_THREADS, 0, s>>>(static_cast<const uint16_t*>(o),
+                                      static_cast<const uint16_t*>(dO), delta, p.T, p.Hq, n_rows);
   return hipGetLastError();
 }
 
@@ -118,7 +132,8 @@ hipError_t launch_bwd_rope_prep_e(const Problem& p, const void* o, const void* d
   const int nb = (int)((n_q + PRE_ROWS - 1) / PRE_ROWS);
   const int nbk = (int)((n_k + PRE_ROWS - 1) / PRE_ROWS);
   const dim3 grid((unsigned)(2 * nb + nbk));
-  attn_bwd_rope_prep_kernel<E><<<grid, PRE_THREADS, 0, s>>>(
+  auto kernel = p.D == 128 ? attn_bwd_rope_prep_kernel<E, 128> : attn_bwd_rope_prep_kernel<E, 64>;
+  kernel<<<grid, PRE_THREADS, 0, s>>>(
       static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO),
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rcos, rsin, delta,
       static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), p.T, p.Hq, p.Hkv, n_q, n_k, nb);

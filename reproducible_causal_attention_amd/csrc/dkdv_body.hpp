@@ -33,6 +33,11 @@
 //   * each wave parks its partial in its own LDS region; the eight partials are
 //     summed in wave order 0..7 and written once (dK scaled by the softmax
 //     scale), in bf16 with round to nearest even.
+// With 128-wide heads the rows of a step are twice as long, so each wave has
+// one step buffer instead of two (the next step's copy is issued once the
+// current one has been read), K^T and V^T are read from LDS at every step
+// instead of being held in registers, and the dK and dV partials are parked
+// and summed one after the other.
 #pragma once
 
 #include "cdna4.hpp"
@@ -43,20 +48,32 @@ namespace dkdv {
 
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int ROWS_BYTES = 32 * 128;                   // 32 swizzled rows of 64 bf16
-constexpr int BUF_BYTES = 2 * ROWS_BYTES + 256;        // q rows, dO rows, 64 row statistics
-constexpr int WAVE_BYTES = 2 * BUF_BYTES;              // double-buffered
-constexpr int KV_OFF = NWAVES * WAVE_BYTES;            // staging of the block's K and V rows
-constexpr int SMEM_BYTES = KV_OFF + 2 * ROWS_BYTES;
-static_assert(16 * 64 * 16 <= WAVE_BYTES, "a wave's partial dK, dV must fit its region");
-static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
+constexpr int HALF_BYTES = 32 * 128;  // 32 swizzled rows of 64 elements
+
+// Head-dimension dependent layout (kD = 64 or 128): a block of 32 rows is kD/64
+// swizzled 64-column halves one after the other.
+template <int kD>
+struct Dims {
+  static constexpr int NH = kD / 64, NQ = kD / 16, ND = kD / 32;
+  static constexpr int ROWS_BYTES = NH * HALF_BYTES;
+  static constexpr int BUF_BYTES = 2 * ROWS_BYTES + 256;  // q rows, dO rows, 64 row statistics
+  static constexpr int NBUF = kD == 64 ? 2 : 1;           // step buffers per wave
+  static constexpr int WAVE_BYTES = NBUF * BUF_BYTES;
+  static constexpr int KV_OFF = NWAVES * WAVE_BYTES;      // staging of the block's K and V rows
+  static constexpr int SMEM_BYTES = KV_OFF + 2 * ROWS_BYTES;
+  static constexpr bool KV_REGS = kD == 64;               // K^T, V^T held in registers
+  static constexpr int PASSES = kD == 64 ? 1 : 2;         // dK and dV parked together or in turn
+  static_assert(2 * ND * 4 * 64 * 16 / PASSES <= WAVE_BYTES, "a wave's parked partial must fit its region");
+  static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
+};
+constexpr int SMEM_BYTES = Dims<64>::SMEM_BYTES;  // the 64-column kernels
 
 // The work of unit `unit` (a pair of key blocks of one (batch, KV head), see
 // decode_unit) for a 512-thread workgroup; smem holds SMEM_BYTES.
 // kRope: q and k are the rotated q', k' (rotary embedding); the epilogue maps
 // dK back through each pair's rotation transpose with the tables rcos, rsin
-// ([T, 32] float32), so dk is the gradient with respect to the unrotated k.
-template <class E, bool kRope>
+// ([T, kD/2] float32), so dk is the gradient with respect to the unrotated k.
+template <class E, bool kRope, int kD>
 __device__ __forceinline__ void unit_body(
     char* __restrict__ smem, int unit, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -64,6 +81,11 @@ __device__ __forceinline__ void unit_body(
     const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
     int causal) {
+  using Dm = Dims<kD>;
+  constexpr int NH = Dm::NH, NQ = Dm::NQ, ND = Dm::ND, ROWS_BYTES = Dm::ROWS_BYTES;
+  constexpr int BUF_BYTES = Dm::BUF_BYTES, WAVE_BYTES = Dm::WAVE_BYTES, KV_OFF = Dm::KV_OFF;
+  constexpr int HALF_ELEMS = HALF_BYTES / 2;
+  constexpr uint32_t kHalf = kD / 2;  // rotary pairs per row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
@@ -78,9 +100,9 @@ __device__ __forceinline__ void unit_body(
   const int G = Hq / Hkv;
 
   // Per-batch-element buffers; byte offsets below are within one batch element.
-  const uint32_t q_row = (uint32_t)Hq * kHeadDim * 2;   // bytes between tokens of q / dO
-  const uint32_t kv_row = (uint32_t)Hkv * kHeadDim * 2;  // bytes between tokens of k / v
-  const size_t qe = (size_t)T * Hq * kHeadDim, ke = (size_t)T * Hkv * kHeadDim;
+  const uint32_t q_row = (uint32_t)Hq * kD * 2;   // bytes between tokens of q / dO
+  const uint32_t kv_row = (uint32_t)Hkv * kD * 2;  // bytes between tokens of k / v
+  const size_t qe = (size_t)T * Hq * kD, ke = (size_t)T * Hkv * kD;
   const rsrc_t rdk = make_rsrc(dk + b * ke, (uint32_t)T * kv_row);
   const rsrc_t rdv = make_rsrc(dv + b * ke, (uint32_t)T * kv_row);
   const u32x4_t q_src = raw_rsrc(q + b * qe, (uint32_t)T * q_row);   // load-to-LDS sources
@@ -121,52 +143,64 @@ __device__ __forceinline__ void unit_body(
       const int qb = qb0 + (s - hh * per_head);
       const int h = kvh * G + hh;
       char* dst = my_region + buf * BUF_BYTES;
-      const uint32_t step_off = (uint32_t)(32 * qb) * q_row + (uint32_t)h * kHeadDim * 2;  // scalar
+      const uint32_t step_off = (uint32_t)(32 * qb) * q_row + (uint32_t)h * kD * 2;  // scalar
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dma16s(q_src, dst + 1024 * i, row_off[i], step_off);
-        dma16s(do_src, dst + ROWS_BYTES + 1024 * i, row_off[i], step_off);
+      for (int c = 0; c < NH; ++c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dma16s(q_src, dst + c * HALF_BYTES + 1024 * i, row_off[i] + 128 * c, step_off);
+          dma16s(do_src, dst + ROWS_BYTES + c * HALF_BYTES + 1024 * i, row_off[i] + 128 * c, step_off);
+        }
       }
       const uint32_t soff = ((uint32_t)h * T + 32 * qb + l32) * 4;
       l_raw = bload_f32(rl, soff);
       d_raw = bload_f32(rd, soff);
     };
 
-    // Prologue: K and V rows of the block (wave w copies eight rows of K for
-    // w < 4, of V for w >= 4) and this wave's first step.
+    // Prologue: K and V rows of the block (copy instruction i = (tensor,
+    // 64-column half, group of eight rows) is issued by wave i % 8) and this
+    // wave's first step.
     float l_raw = 0.f, d_raw = 0.f;
-    {
-      const int r = 8 * (wave & 3) + dma_row;
-      const uint32_t off = (uint32_t)(k0 + r) * kv_row + (uint32_t)kvh * kHeadDim * 2 + dma_chunk_bytes(r);
-      char* dst = smem + KV_OFF + (wave >> 2) * ROWS_BYTES + 1024 * (wave & 3);
-      dma16(wave < 4 ? k_src : v_src, dst, off);
+#pragma unroll
+    for (int i = wave; i < 8 * NH; i += NWAVES) {
+      const int t = i / (4 * NH), c = (i / 4) % NH, rg = i % 4;
+      const int r = 8 * rg + dma_row;
+      const uint32_t off = (uint32_t)(k0 + r) * kv_row + (uint32_t)kvh * kD * 2 + 128 * c + dma_chunk_bytes(r);
+      char* dst = smem + KV_OFF + t * ROWS_BYTES + c * HALF_BYTES + 1024 * rg;
+      dma16(t == 0 ? k_src : v_src, dst, off);
     }
     if (wave < nsteps) issue_step(wave, 0, l_raw, d_raw);
     wait_loads();
     __syncthreads();
 
-    // K^T and V^T as B operands (keys on the lanes): d = 16c + 8g + [0, 8).
-    u32x4_t kf[4], vf[4];
+    // K^T and V^T as B operands (keys on the lanes): d = 16c + 8g + [0, 8), held in
+    // registers for 64-wide heads, read from LDS at every step otherwise.
+    auto k_operand = [&](int c) { return lds_load16_swz(sK + (c >> 2) * HALF_ELEMS, l32, 16 * (c & 3) + 8 * g); };
+    auto v_operand = [&](int c) { return lds_load16_swz(sV + (c >> 2) * HALF_ELEMS, l32, 16 * (c & 3) + 8 * g); };
+    u32x4_t kf[Dm::KV_REGS ? NQ : 1], vf[Dm::KV_REGS ? NQ : 1];
+    if (Dm::KV_REGS) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      kf[c] = lds_load16_swz(sK, l32, 16 * c + 8 * g);
-      vf[c] = lds_load16_swz(sV, l32, 16 * c + 8 * g);
+      for (int c = 0; c < NQ; ++c) {
+        kf[c] = k_operand(c);
+        vf[c] = v_operand(c);
+      }
     }
-    f32x16_t dk_acc[2] = {zero16(), zero16()};  // dK^T: rows d = 32*db + 8*(r/4) + 4g + r%4
-    f32x16_t dv_acc[2] = {zero16(), zero16()};
+    f32x16_t dk_acc[ND], dv_acc[ND];  // dK^T: rows d = 32*db + 8*(r/4) + 4g + r%4
+#pragma unroll
+    for (int db = 0; db < ND; ++db) dk_acc[db] = dv_acc[db] = zero16();
 
     int buf = 0;
     for (int s = wave; s < nsteps; s += NWAVES, buf ^= 1) {
       const int hh = s / per_head;
       const int q0 = 32 * (qb0 + (s - hh * per_head));
-      char* cur = my_region + buf * BUF_BYTES;
+      char* cur = my_region + (Dm::NBUF == 2 ? buf : 0) * BUF_BYTES;
       const uint16_t* sQ = reinterpret_cast<const uint16_t*>(cur);
       const uint16_t* sdO = reinterpret_cast<const uint16_t*>(cur + ROWS_BYTES);
       float* stat = reinterpret_cast<float*>(cur + 2 * ROWS_BYTES);  // [0,32): lse*log2e, [32,64): -delta
 
       wait_loads();  // this step's rows and statistics (issued one step ago)
       stat[lane] = g == 0 ? l_raw * kLog2e : -d_raw;
-      if (s + NWAVES < nsteps) issue_step(s + NWAVES, buf ^ 1, l_raw, d_raw);
+      if (Dm::NBUF == 2 && s + NWAVES < nsteps) issue_step(s + NWAVES, buf ^ 1, l_raw, d_raw);
       wave_lds_fence();
 
       // Register r of a 32x32 accumulator is query q0 + 8*(r/4) + 4g + r%4
@@ -181,9 +215,10 @@ __device__ __forceinline__ void unit_body(
       }
       f32x16_t sacc = zero16();
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        sacc = E::mfma(lds_load16_swz(sQ, l32, 16 * c + 8 * g), kf[c], sacc);
-        pacc = E::mfma(lds_load16_swz(sdO, l32, 16 * c + 8 * g), vf[c], pacc);
+      for (int c = 0; c < NQ; ++c) {
+        const int ho = (c >> 2) * HALF_ELEMS, col = 16 * (c & 3) + 8 * g;
+        sacc = E::mfma(lds_load16_swz(sQ + ho, l32, col), Dm::KV_REGS ? kf[c] : k_operand(c), sacc);
+        pacc = E::mfma(lds_load16_swz(sdO + ho, l32, col), Dm::KV_REGS ? vf[c] : v_operand(c), pacc);
       }
       // pacc now holds dP - delta.
       if ((causal && q0 == k0) || q0 + 31 >= T) {
@@ -208,64 +243,81 @@ __device__ __forceinline__ void unit_body(
       const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
       const u32x4_t sb0 = pack_operand_e<E>(pacc, 0), sb1 = pack_operand_e<E>(pacc, 8);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        dv_acc[db] = E::mfma(lds_operand_T_swz(sdO, 0, 32 * db, lane), pb0, dv_acc[db]);
-        dk_acc[db] = E::mfma(lds_operand_T_swz(sQ, 0, 32 * db, lane), sb0, dk_acc[db]);
-        dv_acc[db] = E::mfma(lds_operand_T_swz(sdO, 16, 32 * db, lane), pb1, dv_acc[db]);
-        dk_acc[db] = E::mfma(lds_operand_T_swz(sQ, 16, 32 * db, lane), sb1, dk_acc[db]);
+      for (int db = 0; db < ND; ++db) {
+        const uint16_t* sdOh = sdO + (db >> 1) * HALF_ELEMS;
+        const uint16_t* sQh = sQ + (db >> 1) * HALF_ELEMS;
+        const int c0 = 32 * (db & 1);
+        dv_acc[db] = E::mfma(lds_operand_T_swz(sdOh, 0, c0, lane), pb0, dv_acc[db]);
+        dk_acc[db] = E::mfma(lds_operand_T_swz(sQh, 0, c0, lane), sb0, dk_acc[db]);
+        dv_acc[db] = E::mfma(lds_operand_T_swz(sdOh, 16, c0, lane), pb1, dv_acc[db]);
+        dk_acc[db] = E::mfma(lds_operand_T_swz(sQh, 16, c0, lane), sb1, dk_acc[db]);
       }
       wave_lds_fence();  // this buffer's reads complete before it is refilled
+      if (Dm::NBUF == 1 && s + NWAVES < nsteps) issue_step(s + NWAVES, 0, l_raw, d_raw);
     }
 
     // Sum the eight partials in wave order and write dK (scaled) and dV once.
     // Each wave stores its partial in its own region as soon as its last step
-    // is done: [float4 index f][lane], f = 0..7 dK, 8..15 dV, float4 f of a
-    // tensor being accumulator registers 4f .. 4f+3 of the flat 32.
-    {
+    // is done: [float4 index f][lane], float4 f of a tensor being accumulator
+    // registers 4f .. 4f+3 of the flat 16*ND; for 64-wide heads dK at f and dV
+    // at 4*ND + f in one pass, otherwise dK in the first pass and dV in the second.
+#pragma unroll
+    for (int pass = 0; pass < Dm::PASSES; ++pass) {
+      if (pass > 0) __syncthreads();  // every wave has read the first pass's partials
       float4* mine = reinterpret_cast<float4*>(my_region);
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const f32x16_t& a = dk_acc[f >> 2];
-        const f32x16_t& c = dv_acc[f >> 2];
+      for (int f = 0; f < 4 * ND; ++f) {
         const int r = 4 * (f & 3);
-        mine[f * 64 + lane] = make_float4(a[r], a[r + 1], a[r + 2], a[r + 3]);
-        mine[(8 + f) * 64 + lane] = make_float4(c[r], c[r + 1], c[r + 2], c[r + 3]);
+        if (Dm::PASSES == 1 || pass == 0) {
+          const f32x16_t& a = dk_acc[f >> 2];
+          mine[f * 64 + lane] = make_float4(a[r], a[r + 1], a[r + 2], a[r + 3]);
+        }
+        if (Dm::PASSES == 1 || pass == 1) {
+          const f32x16_t& c = dv_acc[f >> 2];
+          mine[((Dm::PASSES == 1 ? 4 * ND : 0) + f) * 64 + lane] = make_float4(c[r], c[r + 1], c[r + 2], c[r + 3]);
+        }
       }
-    }
-    __syncthreads();
-    {
+      __syncthreads();
       // Thread -> (key kk, d = 4*c4 .. 4*c4+3), which is registers 16*db + r0 .. +3
       // of lane kk + 32*(c4 % 2) with db = c4 / 8, r0 = 4*((c4 % 8) / 2).  One wave
       // covers the 64 lanes of one float4 index, so its LDS reads are consecutive.
       const int src_lane = tid & 63;
       const int kk = tid & 31;
-      const int c4 = 2 * wave + ((tid >> 5) & 1);
-      const int f = 4 * (c4 >> 3) + ((c4 & 7) >> 1);  // = 4*(wave/4) + wave%4
-      const float4* part0 = reinterpret_cast<const float4*>(smem);
-      float4 sk = part0[f * 64 + src_lane], sv = part0[(8 + f) * 64 + src_lane];
 #pragma unroll
-      for (int w = 1; w < NWAVES; ++w) {
-        const float4* part = reinterpret_cast<const float4*>(smem + w * WAVE_BYTES);
-        const float4 xk = part[f * 64 + src_lane];
-        const float4 xv = part[(8 + f) * 64 + src_lane];
-        sk.x += xk.x; sk.y += xk.y; sk.z += xk.z; sk.w += xk.w;
-        sv.x += xv.x; sv.y += xv.y; sv.z += xv.z; sv.w += xv.w;
+      for (int it = 0; it < NH; ++it) {
+        const int c4 = 2 * (wave + NWAVES * it) + ((tid >> 5) & 1);
+        const int f = 4 * (c4 >> 3) + ((c4 & 7) >> 1);
+        const uint32_t out_off = (uint32_t)(k0 + kk) * kv_row + (uint32_t)kvh * kD * 2 + 8 * c4;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {  // 0: dK, 1: dV
+          if (Dm::PASSES == 2 && t != pass) continue;
+          const int fi = (Dm::PASSES == 1 ? t * 4 * ND : 0) + f;
+          float4 acc = reinterpret_cast<const float4*>(smem)[fi * 64 + src_lane];
+#pragma unroll
+          for (int w = 1; w < NWAVES; ++w) {
+            const float4 x = reinterpret_cast<const float4*>(smem + w * WAVE_BYTES)[fi * 64 + src_lane];
+            acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+          }
+          u32x2_t out;
+          if (t == 0) {
+            float g0 = acc.x * scale, g1 = acc.y * scale, g2 = acc.z * scale, g3 = acc.w * scale;
+            if (kRope) {  // d = 4*c4 .. +3: pairs 2*c4, 2*c4 + 1 of key k0 + kk
+              const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * kHalf * 4u);
+              const rsrc_t rts = make_rsrc(rsin, (uint32_t)T * kHalf * 4u);
+              const uint32_t toff = ((uint32_t)(k0 + kk) * kHalf + 2 * c4) * 4;
+              rope_rotate_back(g0, g1, bload_f32(rtc, toff), bload_f32(rts, toff));
+              rope_rotate_back(g2, g3, bload_f32(rtc, toff + 4), bload_f32(rts, toff + 4));
+            }
+            out[0] = E::pack2(g0, g1);
+            out[1] = E::pack2(g2, g3);
+            bstore8(rdk, out_off, out);  // rows past the sequence end are dropped
+          } else {
+            out[0] = E::pack2(acc.x, acc.y);
+            out[1] = E::pack2(acc.z, acc.w);
+            bstore8(rdv, out_off, out);
+          }
+        }
       }
-      const uint32_t out_off = (uint32_t)(k0 + kk) * kv_row + (uint32_t)kvh * kHeadDim * 2 + 8 * c4;
-      u32x2_t ok, ov;
-      float g0 = sk.x * scale, g1 = sk.y * scale, g2 = sk.z * scale, g3 = sk.w * scale;
-      if (kRope) {  // d = 4*c4 .. +3: pairs 2*c4, 2*c4 + 1 of key k0 + kk
-        const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * 128u), rts = make_rsrc(rsin, (uint32_t)T * 128u);
-        const uint32_t toff = ((uint32_t)(k0 + kk) * 32 + 2 * c4) * 4;
-        rope_rotate_back(g0, g1, bload_f32(rtc, toff), bload_f32(rts, toff));
-        rope_rotate_back(g2, g3, bload_f32(rtc, toff + 4), bload_f32(rts, toff + 4));
-      }
-      ok[0] = E::pack2(g0, g1);
-      ok[1] = E::pack2(g2, g3);
-      ov[0] = E::pack2(sv.x, sv.y);
-      ov[1] = E::pack2(sv.z, sv.w);
-      bstore8(rdk, out_off, ok);  // rows past the sequence end are dropped
-      bstore8(rdv, out_off, ov);
     }
     __syncthreads();  // the regions are refilled by the next block
   }

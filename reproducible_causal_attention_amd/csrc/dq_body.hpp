@@ -34,24 +34,34 @@ constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per LDS tile
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int TILE_BYTES = BN * 128;  // one K or V tile: 64 swizzled rows of 64 bf16
-static_assert(4 * 8 * 64 * 16 <= 4 * TILE_BYTES, "reduction buffer must fit");
-static_assert(2 * BN * 8 == NWAVES * 64 * 2, "a tile pair is two load-to-LDS instructions per wave");
+constexpr int HALF_BYTES = BN * 128;  // 64 swizzled rows of 64 elements: columns 64c .. 64c+63
+static_assert(2 * BN * 8 == NWAVES * 64 * 2, "a tile pair is two load-to-LDS instructions per wave per 64 columns");
 
-constexpr int SMEM_BYTES = 4 * TILE_BYTES;  // [buffer][K, V]
+// One K or V tile of kD columns is kD/64 such halves one after the other.
+template <int kD>
+struct Dims {
+  static constexpr int TILE_BYTES = (kD / 64) * HALF_BYTES;
+  static constexpr int SMEM_BYTES = 4 * TILE_BYTES;  // [buffer][K, V]
+  static constexpr int NQ = kD / 16, ND = kD / 32, NH = kD / 64;
+  static_assert(4 * (4 * ND) * 64 * 16 <= SMEM_BYTES, "reduction buffer must fit");
+};
+constexpr int SMEM_BYTES = Dims<64>::SMEM_BYTES;  // the 64-column kernels
 
 // The work of unit `unit` (one 128-row query tile of one (batch, query head),
 // see decode_unit) for a 512-thread workgroup; smem holds SMEM_BYTES.
 // kRope: q and k are the rotated q', k' (rotary embedding); the epilogue maps
 // dQ back through each pair's rotation transpose with the tables rcos, rsin
-// ([T, 32] float32), so dq is the gradient with respect to the unrotated q.
-template <class E, bool kRope>
+// ([T, kD/2] float32), so dq is the gradient with respect to the unrotated q.
+template <class E, bool kRope, int kD>
 __device__ __forceinline__ void unit_body(
     char* __restrict__ smem, int unit, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dq,
     int B, int T, int Hq, int Hkv, float scale, float scale_log2, int causal) {
+  using Dm = Dims<kD>;
+  constexpr int TILE_BYTES = Dm::TILE_BYTES, NQ = Dm::NQ, ND = Dm::ND, NH = Dm::NH;
+  constexpr uint32_t kHalf = kD / 2;  // rotary pairs per row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
@@ -71,23 +81,23 @@ __device__ __forceinline__ void unit_body(
   const int h = kvh * G + hh;
 
   // Per-batch-element buffers; byte offsets below are within one batch element.
-  const uint32_t q_row = (uint32_t)Hq * kHeadDim * 2;   // bytes between tokens of q / o
-  const uint32_t kv_row = (uint32_t)Hkv * kHeadDim * 2;  // bytes between tokens of k / v
-  const size_t qe = (size_t)T * Hq * kHeadDim, ke = (size_t)T * Hkv * kHeadDim;
+  const uint32_t q_row = (uint32_t)Hq * kD * 2;   // bytes between tokens of q / o
+  const uint32_t kv_row = (uint32_t)Hkv * kD * 2;  // bytes between tokens of k / v
+  const size_t qe = (size_t)T * Hq * kD, ke = (size_t)T * Hkv * kD;
   const u32x4_t k_src = raw_rsrc(k + b * ke, (uint32_t)T * kv_row);  // load-to-LDS sources
   const u32x4_t v_src = raw_rsrc(v + b * ke, (uint32_t)T * kv_row);
 
   const int qw0 = qt * BM + 32 * qb;  // first query row of this wave
   const int my_q = qw0 + l32;
-  const uint32_t qoff = (uint32_t)my_q * q_row + (uint32_t)h * kHeadDim * 2;  // bytes
+  const uint32_t qoff = (uint32_t)my_q * q_row + (uint32_t)h * kD * 2;  // bytes
 
   // Q^T and dO^T as B operands (queries on the lanes).
   const rsrc_t rq = make_rsrc(q + b * qe, (uint32_t)T * q_row);
   const rsrc_t rdo = make_rsrc(dO + b * qe, (uint32_t)T * q_row);
   const rsrc_t rdq = make_rsrc(dq + b * qe, (uint32_t)T * q_row);
-  u32x4_t qf[4], df[4];
+  u32x4_t qf[NQ], df[NQ];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < NQ; ++s) {
     qf[s] = bload16(rq, qoff + 32 * s + 16 * g);
     df[s] = bload16(rdo, qoff + 32 * s + 16 * g);
   }
@@ -99,22 +109,27 @@ __device__ __forceinline__ void unit_body(
   const float lse_raw = bload_f32(rl, my_q < T ? stat_off : 0xffffffffu);
   const float Dl = bload_f32(rdl, my_q < T ? stat_off : 0xffffffffu);
 
-  f32x16_t dq_acc[2] = {zero16(), zero16()};  // dQ^T: rows d = 32*db + 8*(r/4) + 4g + r%4
+  f32x16_t dq_acc[ND];  // dQ^T: rows d = 32*db + 8*(r/4) + 4g + r%4
+#pragma unroll
+  for (int db = 0; db < ND; ++db) dq_acc[db] = zero16();
 
   const int kv_end = causal ? min(T, (qt + 1) * BM) : T;
   const int n_kv = (kv_end + BN - 1) / BN;
 
-  // Tile copy: wave w copies rows 8w .. 8w+7 of the K tile and of the V tile;
-  // lane fills slot lane % 8 of row 8w + lane / 8 (rows past the sequence end
-  // read as zero).
+  // Tile copy: wave w copies rows 8w .. 8w+7 of every 64-column half of the K
+  // tile and of the V tile; lane fills slot lane % 8 of row 8w + lane / 8 (rows
+  // past the sequence end read as zero).
   const int cp_row = 8 * wave + (lane >> 3);
-  const uint32_t cp_off = (uint32_t)cp_row * kv_row + (uint32_t)kvh * kHeadDim * 2 +
+  const uint32_t cp_off = (uint32_t)cp_row * kv_row + (uint32_t)kvh * kD * 2 +
                           16u * (uint32_t)swz_slot(cp_row, lane & 7);
   auto copy_tile = [&](int kt, int buf) {
     const uint32_t soff = (uint32_t)(kt * BN) * kv_row;  // scalar
     char* dst = smem + (2 * buf) * TILE_BYTES + 1024 * wave;
-    dma16s(k_src, dst, cp_off, soff);
-    dma16s(v_src, dst + TILE_BYTES, cp_off, soff);
+#pragma unroll
+    for (int c = 0; c < NH; ++c) {
+      dma16s(k_src, dst + c * HALF_BYTES, cp_off + 128 * c, soff);
+      dma16s(v_src, dst + TILE_BYTES + c * HALF_BYTES, cp_off + 128 * c, soff);
+    }
   };
 
   copy_tile(0, 0);  // in flight together with the row loads above
@@ -135,9 +150,10 @@ __device__ __forceinline__ void unit_body(
     if (active) {
       f32x16_t sacc = zero16(), pacc = neg_delta;  // dP^T - delta accumulates from -delta
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {  // first product adds to a literal zero
-        const u32x4_t ak = lds_load16_swz(sK, 32 * kh + l32, 16 * s + 8 * g);
-        const u32x4_t av = lds_load16_swz(sV, 32 * kh + l32, 16 * s + 8 * g);
+      for (int s = 0; s < NQ; ++s) {  // first product adds to a literal zero
+        const int hoff = (s >> 2) * (HALF_BYTES / 2);  // elements to the 64-column half
+        const u32x4_t ak = lds_load16_swz(sK + hoff, 32 * kh + l32, 16 * (s & 3) + 8 * g);
+        const u32x4_t av = lds_load16_swz(sV + hoff, 32 * kh + l32, 16 * (s & 3) + 8 * g);
         sacc = E::mfma(ak, qf[s], sacc);
         pacc = E::mfma(av, df[s], pacc);
       }
@@ -157,9 +173,10 @@ __device__ __forceinline__ void unit_body(
       }
       const u32x4_t ds0 = pack_operand_e<E>(pacc, 0), ds1 = pack_operand_e<E>(pacc, 8);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        dq_acc[db] = E::mfma(lds_operand_T_swz(sK, 32 * kh, 32 * db, lane), ds0, dq_acc[db]);
-        dq_acc[db] = E::mfma(lds_operand_T_swz(sK, 32 * kh + 16, 32 * db, lane), ds1, dq_acc[db]);
+      for (int db = 0; db < ND; ++db) {
+        const uint16_t* sKh = sK + (db >> 1) * (HALF_BYTES / 2);
+        dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, 32 * kh, 32 * (db & 1), lane), ds0, dq_acc[db]);
+        dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, 32 * kh + 16, 32 * (db & 1), lane), ds1, dq_acc[db]);
       }
     }
     wait_loads();  // the next tile has landed in LDS
@@ -169,10 +186,10 @@ __device__ __forceinline__ void unit_body(
   // dQ = key half 0 + key half 1, in that order.  Partial of half 1 in LDS as
   // [query block][float4 index f = 4*db + j][lane] (consecutive lanes, no bank
   // conflicts); the last tile's copy has landed and every wave is past its reads.
-  float4* part = reinterpret_cast<float4*>(smem) + qb * 8 * 64 + lane;
+  float4* part = reinterpret_cast<float4*>(smem) + qb * (4 * ND) * 64 + lane;
   if (kh == 1) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+    for (int db = 0; db < ND; ++db) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         part[(4 * db + j) * 64] = make_float4(dq_acc[db][4 * j], dq_acc[db][4 * j + 1],
@@ -182,7 +199,7 @@ __device__ __forceinline__ void unit_body(
   __syncthreads();
   if (kh == 0) {  // rows past the sequence end are dropped by the buffer range check
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+    for (int db = 0; db < ND; ++db) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float4 x = part[(4 * db + j) * 64];
@@ -190,8 +207,9 @@ __device__ __forceinline__ void unit_body(
         float g0 = (dq_acc[db][4 * j + 0] + x.x) * scale, g1 = (dq_acc[db][4 * j + 1] + x.y) * scale;
         float g2 = (dq_acc[db][4 * j + 2] + x.z) * scale, g3 = (dq_acc[db][4 * j + 3] + x.w) * scale;
         if (kRope) {  // d = 32db + 8j + 4g + 0..3: pairs 16db + 4j + 2g + 0, 1 of row my_q
-          const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * 128u), rts = make_rsrc(rsin, (uint32_t)T * 128u);
-          const uint32_t toff = ((uint32_t)my_q * 32 + 16 * db + 4 * j + 2 * g) * 4;
+          const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * kHalf * 4u);
+          const rsrc_t rts = make_rsrc(rsin, (uint32_t)T * kHalf * 4u);
+          const uint32_t toff = ((uint32_t)my_q * kHalf + 16 * db + 4 * j + 2 * g) * 4;
           rope_rotate_back(g0, g1, bload_f32(rtc, toff), bload_f32(rts, toff));
           rope_rotate_back(g2, g3, bload_f32(rtc, toff + 4), bload_f32(rts, toff + 4));
         }

@@ -38,21 +38,32 @@ namespace {
 
 constexpr int BM = 128;    // query rows per workgroup
 constexpr int BN = 64;     // key rows per LDS tile
-constexpr int PITCH = 72;  // LDS row pitch in bf16 elements (144 bytes)
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int TILE = BN * PITCH;
-constexpr int PART_STRIDE = 36;  // floats per lane in the merge buffer (32 of O, m, l)
 constexpr float kSlack = 8.0f;   // lazy-rescale threshold, base-2 units
-static_assert(4 * 64 * PART_STRIDE * 4 <= 4 * TILE * 2, "merge buffer must fit");
+
+// Head-dimension dependent sizes (kD = 64 or 128).
+template <int kD>
+struct Dims {
+  static constexpr int PITCH = kD + 8;           // LDS row pitch in elements (144 / 272 bytes)
+  static constexpr int TILE = BN * PITCH;        // one K or V tile
+  static constexpr int PART_STRIDE = kD / 2 + 4;  // floats per lane in the merge buffer (O, m, l)
+  static constexpr int NQ = kD / 16;             // 16-wide chunks of d: MFMA k-steps of S
+  static constexpr int ND = kD / 32;             // 32-row blocks of O^T
+  static constexpr int NL = kD / 64;             // 16-byte tile loads per thread per tensor
+  static_assert(4 * 64 * PART_STRIDE * 4 <= 4 * TILE * 2, "merge buffer must fit");
+};
 
 // kRope: q and k are rotated as they are loaded (rotary tables rcos, rsin:
-// [T, 32] float32, pair i of position t at t*32 + i), v is not.
-template <bool kPosScale, class E, bool kRope>
+// [T, kD/2] float32, pair i of position t at t*kD/2 + i), v is not.
+template <bool kPosScale, class E, bool kRope, int kD>
 __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ o,
     float* __restrict__ lse, int B, int T, int Hq, int Hkv, float scale_log2, int causal) {
+  using Dm = Dims<kD>;
+  constexpr int PITCH = Dm::PITCH, TILE = Dm::TILE, NQ = Dm::NQ, ND = Dm::ND, NL = Dm::NL;
+  constexpr uint32_t kHalf = kD / 2;  // rotary pairs per row
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
@@ -74,72 +85,84 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
   const int h = kvh * G + hh;
 
   // Per-batch-element buffers; byte offsets below are within one batch element.
-  const uint32_t q_row = (uint32_t)Hq * kHeadDim * 2;   // bytes between tokens of q / o
-  const uint32_t kv_row = (uint32_t)Hkv * kHeadDim * 2;  // bytes between tokens of k / v
-  const size_t qe = (size_t)T * Hq * kHeadDim, ke = (size_t)T * Hkv * kHeadDim;
+  const uint32_t q_row = (uint32_t)Hq * kD * 2;   // bytes between tokens of q / o
+  const uint32_t kv_row = (uint32_t)Hkv * kD * 2;  // bytes between tokens of k / v
+  const size_t qe = (size_t)T * Hq * kD, ke = (size_t)T * Hkv * kD;
   const rsrc_t rk = make_rsrc(k + b * ke, (uint32_t)T * kv_row);
   const rsrc_t rv = make_rsrc(v + b * ke, (uint32_t)T * kv_row);
 
   const int qw0 = qt * BM + 32 * qb;  // first query row of this wave
   const int my_q = qw0 + l32;         // the query row this lane accumulates
-  const uint32_t qoff = (uint32_t)my_q * q_row + (uint32_t)h * kHeadDim * 2;  // bytes
+  const uint32_t qoff = (uint32_t)my_q * q_row + (uint32_t)h * kD * 2;  // bytes
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query my_q, d = 16s + 8g + [0, 8).
   const rsrc_t rq = make_rsrc(q + b * qe, (uint32_t)T * q_row);
   const rsrc_t ro = make_rsrc(o + b * qe, (uint32_t)T * q_row);
   const rsrc_t rl = make_rsrc(lse + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
-  u32x4_t qf[4];
+  u32x4_t qf[NQ];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qf[s] = bload16(rq, qoff + 32 * s + 16 * g);
+  for (int s = 0; s < NQ; ++s) qf[s] = bload16(rq, qoff + 32 * s + 16 * g);
   // Rotary tables (rows past the sequence end read as zero, like their q and k rows).
-  const rsrc_t rtc = make_rsrc(rcos, kRope ? (uint32_t)T * 128u : 0u);
-  const rsrc_t rts = make_rsrc(rsin, kRope ? (uint32_t)T * 128u : 0u);
-  u32x4_t qc[4], qsn[4];
+  const rsrc_t rtc = make_rsrc(rcos, kRope ? (uint32_t)T * kHalf * 4u : 0u);
+  const rsrc_t rts = make_rsrc(rsin, kRope ? (uint32_t)T * kHalf * 4u : 0u);
+  u32x4_t qc[NQ], qsn[NQ];
   if (kRope) {  // lane's pairs of chunk s: i = 8s + 4g + 0..3 of row my_q
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qc[s] = bload16(rtc, ((uint32_t)my_q * 32 + 8 * s + 4 * g) * 4);
-      qsn[s] = bload16(rts, ((uint32_t)my_q * 32 + 8 * s + 4 * g) * 4);
+    for (int s = 0; s < NQ; ++s) {
+      qc[s] = bload16(rtc, ((uint32_t)my_q * kHalf + 8 * s + 4 * g) * 4);
+      qsn[s] = bload16(rts, ((uint32_t)my_q * kHalf + 8 * s + 4 * g) * 4);
     }
   }
   wait_loads();
   if (kRope) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NQ; ++s) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         qf[s][e] = rope_rotate<E>(qf[s][e], bits_to_float(qc[s][e]), bits_to_float(qsn[s][e]));
     }
   }
 
-  f32x16_t oacc[2] = {zero16(), zero16()};  // O^T: rows d = 32*db + 8*(r/4) + 4g + r%4
+  f32x16_t oacc[ND];  // O^T: rows d = 32*db + 8*(r/4) + 4g + r%4
+#pragma unroll
+  for (int db = 0; db < ND; ++db) oacc[db] = zero16();
   float m_run = -1e30f;                     // running max (base-2 units)
   float l_run = 0.f;                        // this lane's share of the running sum
 
   const int kv_end = causal ? min(T, (qt + 1) * BM) : T;
   const int n_kv = (kv_end + BN - 1) / BN;
 
+  // Tile loads: thread -> row ld_row, columns ld_col + 64c + 0..7 for c < NL.
   const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
-  const uint32_t ld_off = (uint32_t)ld_row * kv_row + (uint32_t)kvh * kHeadDim * 2 + 2 * ld_col;
-  u32x4_t kreg, vreg, kc, ksn;
+  const uint32_t ld_off = (uint32_t)ld_row * kv_row + (uint32_t)kvh * kD * 2 + 2 * ld_col;
+  u32x4_t kreg[NL], vreg[NL], kc[NL], ksn[NL];
   auto gload_tile = [&](int kt) {  // rows past the sequence end read as zero
     const uint32_t off = ld_off + (uint32_t)(kt * BN) * kv_row;
-    kreg = bload16(rk, off);
-    vreg = bload16(rv, off);
-    if (kRope) {  // pairs ld_col/2 + 0..3 of key row kt*BN + ld_row
-      const uint32_t toff = ((uint32_t)(kt * BN + ld_row) * 32 + ld_col / 2) * 4;
-      kc = bload16(rtc, toff);
-      ksn = bload16(rts, toff);
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      kreg[c] = bload16(rk, off + 128 * c);
+      vreg[c] = bload16(rv, off + 128 * c);
+    }
+    if (kRope) {  // pairs ld_col/2 + 32c + 0..3 of key row kt*BN + ld_row
+      const uint32_t toff = ((uint32_t)(kt * BN + ld_row) * kHalf + ld_col / 2) * 4;
+#pragma unroll
+      for (int c = 0; c < NL; ++c) {
+        kc[c] = bload16(rtc, toff + 128 * c);
+        ksn[c] = bload16(rts, toff + 128 * c);
+      }
     }
   };
   auto store_tile = [&](int buf) {
-    if (kRope) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        kreg[e] = rope_rotate<E>(kreg[e], bits_to_float(kc[e]), bits_to_float(ksn[e]));
+    for (int c = 0; c < NL; ++c) {
+      if (kRope) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kreg[c][e] = rope_rotate<E>(kreg[c][e], bits_to_float(kc[c][e]), bits_to_float(ksn[c][e]));
+      }
+      lds_store16(smem + (2 * buf) * TILE + ld_row * PITCH + ld_col + 64 * c, kreg[c]);
+      lds_store16(smem + (2 * buf + 1) * TILE + ld_row * PITCH + ld_col + 64 * c, vreg[c]);
     }
-    lds_store16(smem + (2 * buf) * TILE + ld_row * PITCH + ld_col, kreg);
-    lds_store16(smem + (2 * buf + 1) * TILE + ld_row * PITCH + ld_col, vreg);
   };
 
   gload_tile(0);
@@ -156,7 +179,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
     if (active) {
       f32x16_t sacc = zero16();
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < NQ; ++s)
         sacc = E::mfma(lds_load16(sK + (32 * kh + l32) * PITCH + 16 * s + 8 * g), qf[s], sacc);
       // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.  The
       // tile maximum is taken over the raw scores (the scale is positive; for a
@@ -189,7 +212,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
         const float alpha = fast_exp2(m_run - m_cand);
         l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < ND; ++db) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
@@ -210,7 +233,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) l_run = E::add_pair(pb1[i], E::add_pair(pb0[i], l_run));
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < ND; ++db) {
         oacc[db] = E::mfma(lds_operand_T(sV, PITCH, 32 * kh, 32 * db, lane), pb0, oacc[db]);
         oacc[db] = E::mfma(lds_operand_T(sV, PITCH, 32 * kh + 16, 32 * db, lane), pb1, oacc[db]);
       }
@@ -221,28 +244,28 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
 
   // Merge the key halves: (m, l, O) of half 1 into half 0, in that order.
   float* part = reinterpret_cast<float*>(smem);
-  float* slot = part + (qb * 64 + lane) * PART_STRIDE;
+  float* slot = part + (qb * 64 + lane) * Dm::PART_STRIDE;
   if (kh == 1) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+    for (int db = 0; db < ND; ++db) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4)
         *reinterpret_cast<float4*>(slot + 16 * db + r) =
             make_float4(oacc[db][r], oacc[db][r + 1], oacc[db][r + 2], oacc[db][r + 3]);
     }
-    slot[32] = m_run;
-    slot[33] = l_run;
+    slot[kD / 2] = m_run;
+    slot[kD / 2 + 1] = l_run;
   }
   __syncthreads();
   if (kh == 0) {
-    const float m1 = slot[32], l1 = slot[33];
+    const float m1 = slot[kD / 2], l1 = slot[kD / 2 + 1];
     const float m = fmaxf(m_run, m1);
     const float a0 = fast_exp2(m_run - m), a1 = fast_exp2(m1 - m);
     const float l_tot = halves_sum(l_run * a0 + l1 * a1);
     // Rows past the sequence end are dropped by the buffer range check.
     const float inv = 1.0f / l_tot;
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+    for (int db = 0; db < ND; ++db) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float4 x = *reinterpret_cast<const float4*>(slot + 16 * db + 4 * j);
@@ -261,7 +284,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
 }  // namespace
 
 const char* fwd_bf16_tiles() {
-  return "fwd_bf16{BM=128,BN=64,waves=8(4 query x 2 key),mfma=32x32x16}";
+  return "fwd_bf16{BM=128,BN=64,waves=8(4 query x 2 key),mfma=32x32x16,D=64|128}";
 }
 
 template <class E, bool kRope>
@@ -269,7 +292,11 @@ hipError_t launch_fwd_e(const Problem& p, const void* q, const void* k, const vo
                         const float* rcos, const float* rsin, void* o, float* lse, hipStream_t s) {
   const int n_qt = (p.T + BM - 1) / BM;
   const dim3 grid((unsigned)(n_qt * p.B * p.Hq));
-  auto kernel = p.scale_log2 >= 0.f ? attn_fwd_kernel<true, E, kRope> : attn_fwd_kernel<false, E, kRope>;
+  auto kernel = p.D == 128
+                    ? (p.scale_log2 >= 0.f ? attn_fwd_kernel<true, E, kRope, 128>
+                                           : attn_fwd_kernel<false, E, kRope, 128>)
+                    : (p.scale_log2 >= 0.f ? attn_fwd_kernel<true, E, kRope, 64>
+                                           : attn_fwd_kernel<false, E, kRope, 64>);
   kernel<<<grid, NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), rcos, rsin, static_cast<uint16_t*>(o), lse, p.B, p.T, p.Hq,

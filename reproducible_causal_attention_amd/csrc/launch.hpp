@@ -11,6 +11,7 @@ constexpr int kHeadDim = 64;
 // validated by the C ABI layer (contiguous, 16-byte aligned, non-overlapping).
 struct Problem {
   int B, T, Hq, Hkv;
+  int D;             // head dimension: 64, or 128 for the 16-bit kernels
   float scale;       // softmax scale applied to q.k
   float scale_log2;  // scale * log2(e): scores are kept in base-2 units on the GPU
   int causal;

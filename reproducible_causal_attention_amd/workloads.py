@@ -24,7 +24,8 @@ at the pages' shapes:
   drawn with standard deviation 3 so that the softmax is peaked;
 * ``gqa-1x512-f16``, ``gqa-4x1024-f16`` -- the same shapes with float16 storage
   (the adjacent input type: the same dense peak as bf16);
-* ``gqa-4x1024-noncausal`` -- the headline shape without the causal mask.
+* ``gqa-4x1024-noncausal`` -- the headline shape without the causal mask;
+* ``gqa-4x1024-d128`` -- the headline shape with 128-wide heads (scale 1/sqrt(128)).
 
 Generation recipe: ``numpy.random.Generator(PCG64(seed))``; ``standard_normal``
 in float64 drawn in the order Q, K, V, dO, each in C order of its
@@ -103,6 +104,9 @@ WORKLOADS = {
     "gqa-4x1024-noncausal": Workload("gqa-4x1024-noncausal", 4, 1024, 12, 4, 64, "bf16", seed=3,
                                      causal=False,
                                      description="bf16 GQA 12/4, 4 x 1024, no causal mask"),
+    "gqa-4x1024-d128": Workload("gqa-4x1024-d128", 4, 1024, 12, 4, 128, "bf16", seed=3,
+                                scale=128 ** -0.5,
+                                description="bf16 causal GQA 12/4, 4 x 1024, head dim 128"),
 }
 
 

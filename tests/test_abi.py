@@ -88,8 +88,10 @@ FWD_ERRORS = [
     ("T_too_long", dict(T=(1 << 24) + 1), A.ATTN_ERR_INVALID_ARG),
     ("too_many_tiles", dict(B=1 << 14, T=1 << 16, Hq=8, Hkv=8), A.ATTN_ERR_INVALID_ARG),
     ("batch_element_too_large", dict(B=1, T=1 << 20, Hq=128, Hkv=128), A.ATTN_ERR_INVALID_ARG),
-    ("head_dim_128", dict(D=128), A.ATTN_ERR_UNSUPPORTED),
+    ("head_dim_96", dict(D=96), A.ATTN_ERR_UNSUPPORTED),
+    ("f32_head_dim_128", dict(D=128, dtype=A.ATTN_F32), A.ATTN_ERR_UNSUPPORTED),
     ("unknown_dtype", dict(dtype=7), A.ATTN_ERR_UNSUPPORTED),
+    ("unknown_dtype_but_overlap", dict(dtype=7, o=BASE + 64), A.ATTN_ERR_INVALID_ARG),
     ("o_overlaps_q", dict(o=BASE + 64), A.ATTN_ERR_INVALID_ARG),
     ("lse_overlaps_o", dict(lse=BASE + 48 * MB + 16), A.ATTN_ERR_INVALID_ARG),
     ("o_overlaps_v_tail", dict(o=BASE + 32 * MB + 128 * 2 * 64 * 2 - 16), A.ATTN_ERR_INVALID_ARG),
@@ -102,10 +104,12 @@ def test_fwd_validation(lib, name, over, want):
 
 
 def test_adjacent_buffers_are_not_overlap(lib):
-    """o starting exactly where v ends is legal; make one other argument invalid so
-    that nothing launches, and check the overlap rule did not fire first."""
+    """o starting exactly where v ends is legal, one element earlier is not.  An
+    unknown dtype (checked after the overlap rule, 2-byte elements for the
+    sizes) keeps every call from launching."""
     v_end = BASE + 32 * MB + 1 * 128 * 2 * 64 * 2
-    assert call_fwd(lib, fwd_args(o=v_end, D=128)) == A.ATTN_ERR_UNSUPPORTED
+    assert call_fwd(lib, fwd_args(o=v_end, dtype=7)) == A.ATTN_ERR_UNSUPPORTED
+    assert call_fwd(lib, fwd_args(o=v_end - 16, dtype=7)) == A.ATTN_ERR_INVALID_ARG
 
 
 def bwd_call(lib, **over):
@@ -208,7 +212,7 @@ FWD_ROPE_ERRORS = [
     ("misaligned_sin", dict(sin=BASE + 176 * MB + 4), A.ATTN_ERR_INVALID_ARG),
     ("o_overlaps_cos", dict(o=BASE + 160 * MB + 128 * 32 * 4 - 16), A.ATTN_ERR_INVALID_ARG),
     ("lse_overlaps_sin", dict(lse=BASE + 176 * MB), A.ATTN_ERR_INVALID_ARG),
-    ("head_dim_128", dict(D=128), A.ATTN_ERR_UNSUPPORTED),
+    ("head_dim_96", dict(D=96), A.ATTN_ERR_UNSUPPORTED),
     ("groups_do_not_divide", dict(Hq=3), A.ATTN_ERR_INVALID_ARG),
 ]
 
@@ -219,9 +223,12 @@ def test_fwd_rope_validation(lib, name, over, want):
 
 
 def test_rope_tables_end_where_they_should(lib):
-    """o starting right after the cos table ([T, 32] float32) is not overlap; a
-    bad head dim makes the call fail after the overlap rule, so nothing launches."""
-    assert fwd_rope_call(lib, o=BASE + 160 * MB + 128 * 32 * 4, D=128) == A.ATTN_ERR_UNSUPPORTED
+    """o starting right after the cos table ([T, 32] float32) is not overlap, one
+    float earlier it is; float32 (unsupported by the rotary entry points, and
+    checked after the overlap rule) keeps the calls from launching."""
+    end = BASE + 160 * MB + 128 * 32 * 4
+    assert fwd_rope_call(lib, o=end, dtype=A.ATTN_F32) == A.ATTN_ERR_UNSUPPORTED
+    assert fwd_rope_call(lib, o=end - 16, dtype=A.ATTN_F32) == A.ATTN_ERR_INVALID_ARG
 
 
 def bwd_rope_call(lib, **over):
