@@ -113,25 +113,6 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
       qsn[s] = bload16(rts, ((uint32_t)my_q * kHalf + 8 * s + 4 * g) * 4);
     }
   }
-  wait_loads();
-  if (kRope) {
-#pragma unroll
-    for (int s = 0; s < NQ; ++s) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qf[s][e] = rope_rotate<E>(qf[s][e], bits_to_float(qc[s][e]), bits_to_float(qsn[s][e]));
-    }
-  }
-
-  f32x16_t oacc[ND];  // O^T: rows d = 32*db + 8*(r/4) + 4g + r%4
-#pragma unroll
-  for (int db = 0; db < ND; ++db) oacc[db] = zero16();
-  float m_run = -1e30f;                     // running max (base-2 units)
-  float l_run = 0.f;                        // this lane's share of the running sum
-
-  const int kv_end = causal ? min(T, (qt + 1) * BM) : T;
-  const int n_kv = (kv_end + BN - 1) / BN;
-
   // Tile loads: thread -> row ld_row, columns ld_col + 64c + 0..7 for c < NL.
   const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
   const uint32_t ld_off = (uint32_t)ld_row * kv_row + (uint32_t)kvh * kD * 2 + 2 * ld_col;
@@ -165,7 +146,26 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
     }
   };
 
-  gload_tile(0);
+  gload_tile(0);  // in flight together with the Q rows
+  wait_loads();
+  if (kRope) {
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qf[s][e] = rope_rotate<E>(qf[s][e], bits_to_float(qc[s][e]), bits_to_float(qsn[s][e]));
+    }
+  }
+
+  f32x16_t oacc[ND];  // O^T: rows d = 32*db + 8*(r/4) + 4g + r%4
+#pragma unroll
+  for (int db = 0; db < ND; ++db) oacc[db] = zero16();
+  float m_run = -1e30f;                     // running max (base-2 units)
+  float l_run = 0.f;                        // this lane's share of the running sum
+
+  const int kv_end = causal ? min(T, (qt + 1) * BM) : T;
+  const int n_kv = (kv_end + BN - 1) / BN;
+
   store_tile(0);
   __syncthreads();
 
