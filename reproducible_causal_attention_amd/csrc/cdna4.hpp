@@ -330,4 +330,28 @@ __device__ __forceinline__ void decode_unit(int i, int NG, int& gi, int& r) {
   }
 }
 
+// The forward's order for grids of 256 < n <= 512 workgroups (two per CU):
+// workgroup i and i + 256 land on the same CU, so the first n - 256 CUs of the
+// 256 host two workgroups and the rest one (measured from workgroup timelines
+// on MI355X: 32 CUs per XCD, blocks dealt to XCDs round-robin).  Per XCD the
+// heaviest units go to the CUs that host one workgroup, and the others are
+// paired heaviest with lightest, so no CU holds a heavy unit and a second one.
+// Units keep their XCD as in decode_unit.  Other grids use decode_unit.
+__device__ __forceinline__ void decode_unit_paired(int i, int n, int NG, int& gi, int& r) {
+  if ((NG & 7) != 0 || (n & 7) != 0 || n <= 256 || n > 512) {
+    decode_unit(i, NG, gi, r);
+    return;
+  }
+  const int x = i & 7, slot = i >> 3;  // XCD, and slot within it (32 per round)
+  const int per = n >> 3;              // units per XCD
+  const int dbl = per - 32;            // CUs of this XCD that host two workgroups
+  int k;                               // 0 = heaviest unit of this XCD
+  if (slot >= 32) k = per - 1 - (slot - 32);  // second workgroup of a CU: lightest first
+  else if (slot >= dbl) k = slot - dbl;       // CUs with one workgroup: the heaviest
+  else k = (32 - dbl) + slot;                 // first workgroup of a shared CU: next heaviest
+  const int M = NG >> 3;
+  r = k / M;
+  gi = x + 8 * (k - r * M);
+}
+
 }  // namespace rca

@@ -17,8 +17,10 @@
 //     (batch, KV head), so under the causal mask every workgroup has the same
 //     amount of work (the two blocks see n-j and j+1 query blocks);
 //   * the work of one key block is a fixed list of steps (query head of the
-//     group, 32-query block); wave w takes steps w, w+8, w+16, ... and keeps its
-//     own fp32 partial dK^T, dV^T in accumulator registers;
+//     group, 32-query block); for 64-wide heads the two blocks run at once, the
+//     waves split into two groups sized to the blocks' step counts, and wave w
+//     of a group of W takes its block's steps w, w+W, w+2W, ..., keeping its own
+//     fp32 partial dK^T, dV^T in accumulator registers;
 //   * the 32 query rows of q and dO of a step go straight from HBM into a
 //     wave-private, double-buffered LDS region (buffer_load ... lds, eight whole
 //     rows per instruction, XOR-swizzled 16-byte chunks), issued one step
@@ -30,14 +32,15 @@
 //     dV^T and dK^T with the transposed A operands read by ds_read_b64_tr_b16;
 //   * K and V of the key block are staged once through LDS and held in
 //     registers as the B operands of S and dP;
-//   * each wave parks its partial in its own LDS region; the eight partials are
-//     summed in wave order 0..7 and written once (dK scaled by the softmax
-//     scale), in bf16 with round to nearest even.
+//   * each wave parks its partial in its own LDS region; a block's partials
+//     (those of its wave group) are summed in wave order and written once (dK
+//     scaled by the softmax scale), in bf16 with round to nearest even.
 // With 128-wide heads the rows of a step are twice as long, so each wave has
 // one step buffer instead of two (the next step's copy is issued once the
 // current one has been read), K^T and V^T are read from LDS at every step
-// instead of being held in registers, and the dK and dV partials are parked
-// and summed one after the other.
+// instead of being held in registers, the dK and dV partials are parked and
+// summed one after the other, and the two key blocks take one pass each with
+// all eight waves (both blocks' K and V do not fit in LDS besides the rows).
 #pragma once
 
 #include "cdna4.hpp"
@@ -59,8 +62,9 @@ struct Dims {
   static constexpr int BUF_BYTES = 2 * ROWS_BYTES + 256;  // q rows, dO rows, 64 row statistics
   static constexpr int NBUF = kD == 64 ? 2 : 1;           // step buffers per wave
   static constexpr int WAVE_BYTES = NBUF * BUF_BYTES;
-  static constexpr int KV_OFF = NWAVES * WAVE_BYTES;      // staging of the block's K and V rows
-  static constexpr int SMEM_BYTES = KV_OFF + 2 * ROWS_BYTES;
+  static constexpr int KV_OFF = NWAVES * WAVE_BYTES;      // staging of the blocks' K and V rows
+  static constexpr bool TOGETHER = kD == 64;              // both key blocks of a unit at once
+  static constexpr int SMEM_BYTES = KV_OFF + (TOGETHER ? 4 : 2) * ROWS_BYTES;
   static constexpr bool KV_REGS = kD == 64;               // K^T, V^T held in registers
   static constexpr int PASSES = kD == 64 ? 1 : 2;         // dK and dV parked together or in turn
   static_assert(2 * ND * 4 * 64 * 16 / PASSES <= WAVE_BYTES, "a wave's parked partial must fit its region");
@@ -113,8 +117,6 @@ __device__ __forceinline__ void unit_body(
   const rsrc_t rd = make_rsrc(delta + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
 
   char* const my_region = smem + wave * WAVE_BYTES;
-  const uint16_t* const sK = reinterpret_cast<const uint16_t*>(smem + KV_OFF);
-  const uint16_t* const sV = reinterpret_cast<const uint16_t*>(smem + KV_OFF + ROWS_BYTES);
   // Load-to-LDS lane mapping: lane fills slot lane % 8 of row 8i + lane / 8 of an
   // instruction's eight rows, i.e. it fetches chunk swz_slot(row, lane % 8).
   const int dma_row = lane >> 3;
@@ -125,15 +127,40 @@ __device__ __forceinline__ void unit_body(
 #pragma unroll
   for (int i = 0; i < 4; ++i) row_off[i] = (uint32_t)(8 * i + dma_row) * q_row + dma_chunk_bytes(8 * i + dma_row);
 
-  for (int half = 0; half < 2; ++half) {
-    const int j = half == 0 ? pair : nkb - 1 - pair;
-    if (half == 1 && j == pair) break;  // middle block of an odd count: once only
+  // The unit's key blocks jA = pair and jB = nkb - 1 - pair.  For 64-wide heads
+  // both are processed in one pass: waves [0, w0) take block jA's steps and waves
+  // [w0, 8) block jB's, w0 chosen so the two groups' step counts per wave are as
+  // equal as possible.  For 128-wide heads (no room in LDS for both blocks' K
+  // and V) the blocks take one pass each with all eight waves, as does the
+  // middle block of an odd count.
+  const int jA = pair, jB = nkb - 1 - pair;
+  const bool together = Dm::TOGETHER && jA != jB;
+  const int n_pass = (jA == jB || together) ? 1 : 2;
+  auto steps_of = [&](int jb) { return G * (nkb - (causal ? jb : 0)); };
+  for (int ps = 0; ps < n_pass; ++ps) {
+    const int nb = together ? 2 : 1;       // blocks in this pass
+    const int jfirst = ps == 0 ? jA : jB;  // block of wave group 0
+    int w0 = NWAVES;                       // waves of group 0
+    if (together) {
+      const int s0 = steps_of(jA), s1 = steps_of(jB);
+      int best = 1 << 30;
+      for (int w = 1; w < NWAVES; ++w) {
+        const int c = max((s0 + w - 1) / w, (s1 + NWAVES - w - 1) / (NWAVES - w));
+        if (c < best) { best = c; w0 = w; }
+      }
+    }
+    const int my_b = wave >= w0 ? 1 : 0;
+    const int j = my_b == 0 ? jfirst : jB;
+    const int gw = wave - (my_b ? w0 : 0);            // rank in the wave group
+    const int gs = my_b ? NWAVES - w0 : w0;           // size of the wave group
     const int k0 = 32 * j;
     const int my_key = k0 + l32;
 
     const int qb0 = causal ? j : 0;  // first query block that sees key block j
     const int per_head = nkb - qb0;
     const int nsteps = G * per_head;
+    const uint16_t* const sK = reinterpret_cast<const uint16_t*>(smem + KV_OFF + my_b * 2 * ROWS_BYTES);
+    const uint16_t* const sV = sK + ROWS_BYTES / 2;
 
     // Step s: rows 32*qb .. +31 of query head h of the group.  Issues the copy
     // of its q and dO rows into buffer buf of this wave's region, and returns
@@ -157,19 +184,21 @@ __device__ __forceinline__ void unit_body(
       d_raw = bload_f32(rd, soff);
     };
 
-    // Prologue: K and V rows of the block (copy instruction i = (tensor,
-    // 64-column half, group of eight rows) is issued by wave i % 8) and this
-    // wave's first step.
+    // Prologue: K and V rows of the pass's blocks (copy instruction i = (block,
+    // tensor, 64-column half, group of eight rows) is issued by wave i % 8) and
+    // this wave's first step.
     float l_raw = 0.f, d_raw = 0.f;
 #pragma unroll
-    for (int i = wave; i < 8 * NH; i += NWAVES) {
-      const int t = i / (4 * NH), c = (i / 4) % NH, rg = i % 4;
+    for (int i = wave; i < nb * 8 * NH; i += NWAVES) {
+      const int bb = i / (8 * NH), ii = i % (8 * NH);
+      const int t = ii / (4 * NH), c = (ii / 4) % NH, rg = ii % 4;
       const int r = 8 * rg + dma_row;
-      const uint32_t off = (uint32_t)(k0 + r) * kv_row + (uint32_t)kvh * kD * 2 + 128 * c + dma_chunk_bytes(r);
-      char* dst = smem + KV_OFF + t * ROWS_BYTES + c * HALF_BYTES + 1024 * rg;
+      const int kb = 32 * (bb == 0 ? jfirst : jB);
+      const uint32_t off = (uint32_t)(kb + r) * kv_row + (uint32_t)kvh * kD * 2 + 128 * c + dma_chunk_bytes(r);
+      char* dst = smem + KV_OFF + bb * 2 * ROWS_BYTES + t * ROWS_BYTES + c * HALF_BYTES + 1024 * rg;
       dma16(t == 0 ? k_src : v_src, dst, off);
     }
-    if (wave < nsteps) issue_step(wave, 0, l_raw, d_raw);
+    if (gw < nsteps) issue_step(gw, 0, l_raw, d_raw);
     wait_loads();
     __syncthreads();
 
@@ -190,7 +219,7 @@ __device__ __forceinline__ void unit_body(
     for (int db = 0; db < ND; ++db) dk_acc[db] = dv_acc[db] = zero16();
 
     int buf = 0;
-    for (int s = wave; s < nsteps; s += NWAVES, buf ^= 1) {
+    for (int s = gw; s < nsteps; s += gs, buf ^= 1) {
       const int hh = s / per_head;
       const int q0 = 32 * (qb0 + (s - hh * per_head));
       char* cur = my_region + (Dm::NBUF == 2 ? buf : 0) * BUF_BYTES;
@@ -200,7 +229,7 @@ __device__ __forceinline__ void unit_body(
 
       wait_loads();  // this step's rows and statistics (issued one step ago)
       stat[lane] = g == 0 ? l_raw * kLog2e : -d_raw;
-      if (Dm::NBUF == 2 && s + NWAVES < nsteps) issue_step(s + NWAVES, buf ^ 1, l_raw, d_raw);
+      if (Dm::NBUF == 2 && s + gs < nsteps) issue_step(s + gs, buf ^ 1, l_raw, d_raw);
       wave_lds_fence();
 
       // Register r of a 32x32 accumulator is query q0 + 8*(r/4) + 4g + r%4
@@ -253,10 +282,10 @@ __device__ __forceinline__ void unit_body(
         dk_acc[db] = E::mfma(lds_operand_T_swz(sQh, 16, c0, lane), sb1, dk_acc[db]);
       }
       wave_lds_fence();  // this buffer's reads complete before it is refilled
-      if (Dm::NBUF == 1 && s + NWAVES < nsteps) issue_step(s + NWAVES, 0, l_raw, d_raw);
+      if (Dm::NBUF == 1 && s + gs < nsteps) issue_step(s + gs, 0, l_raw, d_raw);
     }
 
-    // Sum the eight partials in wave order and write dK (scaled) and dV once.
+    // Sum each block's partials and write dK (scaled) and dV once.
     // Each wave stores its partial in its own region as soon as its last step
     // is done: [float4 index f][lane], float4 f of a tensor being accumulator
     // registers 4f .. 4f+3 of the flat 16*ND; for 64-wide heads dK at f and dV
@@ -281,40 +310,44 @@ __device__ __forceinline__ void unit_body(
       // Thread -> (key kk, d = 4*c4 .. 4*c4+3), which is registers 16*db + r0 .. +3
       // of lane kk + 32*(c4 % 2) with db = c4 / 8, r0 = 4*((c4 % 8) / 2).  One wave
       // covers the 64 lanes of one float4 index, so its LDS reads are consecutive.
+      // Block bb's partials are those of its wave group, summed in wave order.
       const int src_lane = tid & 63;
       const int kk = tid & 31;
+      for (int bb = 0; bb < nb; ++bb) {
+        const int w_lo = bb == 0 ? 0 : w0, w_hi = bb == 0 ? w0 : NWAVES;
+        const int kb = 32 * (bb == 0 ? jfirst : jB);
 #pragma unroll
-      for (int it = 0; it < NH; ++it) {
-        const int c4 = 2 * (wave + NWAVES * it) + ((tid >> 5) & 1);
-        const int f = 4 * (c4 >> 3) + ((c4 & 7) >> 1);
-        const uint32_t out_off = (uint32_t)(k0 + kk) * kv_row + (uint32_t)kvh * kD * 2 + 8 * c4;
+        for (int it = 0; it < NH; ++it) {
+          const int c4 = 2 * (wave + NWAVES * it) + ((tid >> 5) & 1);
+          const int f = 4 * (c4 >> 3) + ((c4 & 7) >> 1);
+          const uint32_t out_off = (uint32_t)(kb + kk) * kv_row + (uint32_t)kvh * kD * 2 + 8 * c4;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {  // 0: dK, 1: dV
-          if (Dm::PASSES == 2 && t != pass) continue;
-          const int fi = (Dm::PASSES == 1 ? t * 4 * ND : 0) + f;
-          float4 acc = reinterpret_cast<const float4*>(smem)[fi * 64 + src_lane];
-#pragma unroll
-          for (int w = 1; w < NWAVES; ++w) {
-            const float4 x = reinterpret_cast<const float4*>(smem + w * WAVE_BYTES)[fi * 64 + src_lane];
-            acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
-          }
-          u32x2_t out;
-          if (t == 0) {
-            float g0 = acc.x * scale, g1 = acc.y * scale, g2 = acc.z * scale, g3 = acc.w * scale;
-            if (kRope) {  // d = 4*c4 .. +3: pairs 2*c4, 2*c4 + 1 of key k0 + kk
-              const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * kHalf * 4u);
-              const rsrc_t rts = make_rsrc(rsin, (uint32_t)T * kHalf * 4u);
-              const uint32_t toff = ((uint32_t)(k0 + kk) * kHalf + 2 * c4) * 4;
-              rope_rotate_back(g0, g1, bload_f32(rtc, toff), bload_f32(rts, toff));
-              rope_rotate_back(g2, g3, bload_f32(rtc, toff + 4), bload_f32(rts, toff + 4));
+          for (int t = 0; t < 2; ++t) {  // 0: dK, 1: dV
+            if (Dm::PASSES == 2 && t != pass) continue;
+            const int fi = (Dm::PASSES == 1 ? t * 4 * ND : 0) + f;
+            float4 acc = reinterpret_cast<const float4*>(smem + w_lo * WAVE_BYTES)[fi * 64 + src_lane];
+            for (int w = w_lo + 1; w < w_hi; ++w) {
+              const float4 x = reinterpret_cast<const float4*>(smem + w * WAVE_BYTES)[fi * 64 + src_lane];
+              acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
             }
-            out[0] = E::pack2(g0, g1);
-            out[1] = E::pack2(g2, g3);
-            bstore8(rdk, out_off, out);  // rows past the sequence end are dropped
-          } else {
-            out[0] = E::pack2(acc.x, acc.y);
-            out[1] = E::pack2(acc.z, acc.w);
-            bstore8(rdv, out_off, out);
+            u32x2_t out;
+            if (t == 0) {
+              float g0 = acc.x * scale, g1 = acc.y * scale, g2 = acc.z * scale, g3 = acc.w * scale;
+              if (kRope) {  // d = 4*c4 .. +3: pairs 2*c4, 2*c4 + 1 of key kb + kk
+                const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * kHalf * 4u);
+                const rsrc_t rts = make_rsrc(rsin, (uint32_t)T * kHalf * 4u);
+                const uint32_t toff = ((uint32_t)(kb + kk) * kHalf + 2 * c4) * 4;
+                rope_rotate_back(g0, g1, bload_f32(rtc, toff), bload_f32(rts, toff));
+                rope_rotate_back(g2, g3, bload_f32(rtc, toff + 4), bload_f32(rts, toff + 4));
+              }
+              out[0] = E::pack2(g0, g1);
+              out[1] = E::pack2(g2, g3);
+              bstore8(rdk, out_off, out);  // rows past the sequence end are dropped
+            } else {
+              out[0] = E::pack2(acc.x, acc.y);
+              out[1] = E::pack2(acc.z, acc.w);
+              bstore8(rdv, out_off, out);
+            }
           }
         }
       }

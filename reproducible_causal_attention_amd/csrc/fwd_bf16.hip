@@ -77,7 +77,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
   const int G = Hq / Hkv;
   const int n_qt = (T + BM - 1) / BM;
   int gi, rank;
-  decode_unit(blockIdx.x, B * Hkv, gi, rank);
+  // Two 64-wide workgroups fit a CU (the paired order assumes it); one 128-wide.
+  if (kD == 64)
+    decode_unit_paired(blockIdx.x, gridDim.x, B * Hkv, gi, rank);
+  else
+    decode_unit(blockIdx.x, B * Hkv, gi, rank);
   const int b = gi / Hkv;
   const int kvh = gi - b * Hkv;
   const int hh = rank % G;
