@@ -10,11 +10,12 @@
 // Decomposition (MI355X-first):
 //   * a workgroup of 8 waves owns 128 query rows of one (batch, query head):
 //     four 32-row query blocks times two key halves;
-//   * key/value tiles of 64 rows go straight from HBM into double-buffered LDS
-//     (buffer_load ... lds, eight whole rows per instruction, XOR-swizzled
-//     16-byte chunks; the next tile's copy is in flight while the current one
-//     is used); wave (query block qb, key half kh) uses keys 32*kh .. 32*kh+31
-//     of each tile, so every K/V row in LDS feeds four waves;
+//   * key/value tiles of 128 rows (64 for 128-wide heads) go straight from HBM
+//     into double-buffered LDS (buffer_load ... lds, eight whole rows per
+//     instruction, XOR-swizzled 16-byte chunks; the next tile's copy is in
+//     flight while the current one is used); wave (query block qb, key half kh)
+//     uses the kh-th half of each tile in blocks of 32 keys, so every K/V row in
+//     LDS feeds four waves;
 //   * S^T = K Q^T and dP^T = V dO^T put the queries on the lanes, so lse and
 //     delta are one register per lane, the dP accumulator starts at -delta
 //     (the MFMA adds dO.v to it), and dS^T feeds dQ^T += K^T dS^T directly from
@@ -31,15 +32,19 @@ namespace rca {
 namespace dqb {
 
 constexpr int BM = 128;  // query rows per workgroup
-constexpr int BN = 64;   // keys per LDS tile
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int HALF_BYTES = BN * 128;  // 64 swizzled rows of 64 elements: columns 64c .. 64c+63
-static_assert(2 * BN * 8 == NWAVES * 64 * 2, "a tile pair is two load-to-LDS instructions per wave per 64 columns");
 
-// One K or V tile of kD columns is kD/64 such halves one after the other.
+// Sizes for head dim kD.  A K or V tile of BN keys is kD/64 column halves one
+// after the other, each BN swizzled rows of 64 elements; wave (qb, kh) takes
+// keys kh*BN/2 .. +BN/2-1 of every tile as NB blocks of 32.  64-wide heads use
+// 128-key tiles (half the tiles and barriers per key); 128-wide heads, whose
+// registers are full, 64-key tiles.
 template <int kD>
 struct Dims {
+  static constexpr int BN = kD == 64 ? 128 : 64;
+  static constexpr int NB = BN / 64;                 // 32-key blocks per wave per tile
+  static constexpr int HALF_BYTES = BN * 128;
   static constexpr int TILE_BYTES = (kD / 64) * HALF_BYTES;
   static constexpr int SMEM_BYTES = 4 * TILE_BYTES;  // [buffer][K, V]
   static constexpr int NQ = kD / 16, ND = kD / 32, NH = kD / 64;
@@ -61,6 +66,7 @@ __device__ __forceinline__ void unit_body(
     int B, int T, int Hq, int Hkv, float scale, float scale_log2, int causal) {
   using Dm = Dims<kD>;
   constexpr int TILE_BYTES = Dm::TILE_BYTES, NQ = Dm::NQ, ND = Dm::ND, NH = Dm::NH;
+  constexpr int BN = Dm::BN, NB = Dm::NB, HALF_BYTES = Dm::HALF_BYTES;
   constexpr uint32_t kHalf = kD / 2;  // rotary pairs per row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,19 +122,22 @@ __device__ __forceinline__ void unit_body(
   const int kv_end = causal ? min(T, (qt + 1) * BM) : T;
   const int n_kv = (kv_end + BN - 1) / BN;
 
-  // Tile copy: wave w copies rows 8w .. 8w+7 of every 64-column half of the K
-  // tile and of the V tile; lane fills slot lane % 8 of row 8w + lane / 8 (rows
-  // past the sequence end read as zero).
+  // Tile copy: in pass p wave w copies rows 64p + 8w .. +7 of every 64-column
+  // half of the K tile and of the V tile; lane fills slot lane % 8 of row
+  // 64p + 8w + lane / 8 (rows past the sequence end read as zero).
   const int cp_row = 8 * wave + (lane >> 3);
   const uint32_t cp_off = (uint32_t)cp_row * kv_row + (uint32_t)kvh * kD * 2 +
                           16u * (uint32_t)swz_slot(cp_row, lane & 7);
   auto copy_tile = [&](int kt, int buf) {
-    const uint32_t soff = (uint32_t)(kt * BN) * kv_row;  // scalar
-    char* dst = smem + (2 * buf) * TILE_BYTES + 1024 * wave;
 #pragma unroll
-    for (int c = 0; c < NH; ++c) {
-      dma16s(k_src, dst + c * HALF_BYTES, cp_off + 128 * c, soff);
-      dma16s(v_src, dst + TILE_BYTES + c * HALF_BYTES, cp_off + 128 * c, soff);
+    for (int p = 0; p < BN / 64; ++p) {
+      const uint32_t soff = (uint32_t)(kt * BN + 64 * p) * kv_row;  // scalar
+      char* dst = smem + (2 * buf) * TILE_BYTES + 8192 * p + 1024 * wave;
+#pragma unroll
+      for (int c = 0; c < NH; ++c) {
+        dma16s(k_src, dst + c * HALF_BYTES, cp_off + 128 * c, soff);
+        dma16s(v_src, dst + TILE_BYTES + c * HALF_BYTES, cp_off + 128 * c, soff);
+      }
     }
   };
 
@@ -145,38 +154,42 @@ __device__ __forceinline__ void unit_body(
     if (kt + 1 < n_kv) copy_tile(kt + 1, cur ^ 1);  // that buffer was last read before the previous barrier
     const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + (2 * cur) * TILE_BYTES);
     const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + (2 * cur + 1) * TILE_BYTES);
-    const int kb0 = kt * BN + 32 * kh;  // first key of this wave's half
-    const bool active = kb0 < T && (!causal || kb0 <= qw0 + 31);
-    if (active) {
-      f32x16_t sacc = zero16(), pacc = neg_delta;  // dP^T - delta accumulates from -delta
 #pragma unroll
-      for (int s = 0; s < NQ; ++s) {  // first product adds to a literal zero
-        const int hoff = (s >> 2) * (HALF_BYTES / 2);  // elements to the 64-column half
-        const u32x4_t ak = lds_load16_swz(sK + hoff, 32 * kh + l32, 16 * (s & 3) + 8 * g);
-        const u32x4_t av = lds_load16_swz(sV + hoff, 32 * kh + l32, 16 * (s & 3) + 8 * g);
-        sacc = E::mfma(ak, qf[s], sacc);
-        pacc = E::mfma(av, df[s], pacc);
-      }
-      // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.
-      if ((causal && kb0 + 31 > qw0) || kb0 + 32 > T) {
-        // Diagonal tile or sequence tail: zero P where the key is after the
-        // query or past the end.
+    for (int sb = 0; sb < NB; ++sb) {
+      const int krow = kh * (BN / 2) + 32 * sb;  // first tile row of this 32-key block
+      const int kb0 = kt * BN + krow;            // its first key
+      const bool active = kb0 < T && (!causal || kb0 <= qw0 + 31);
+      if (active) {
+        f32x16_t sacc = zero16(), pacc = neg_delta;  // dP^T - delta accumulates from -delta
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const float p = fast_exp2(fmaf(sacc[r], scale_log2, -L2));
-          pacc[r] *= ((causal && key > my_q) || key >= T) ? 0.f : p;
+        for (int s = 0; s < NQ; ++s) {  // first product adds to a literal zero
+          const int hoff = (s >> 2) * (HALF_BYTES / 2);  // elements to the 64-column half
+          const u32x4_t ak = lds_load16_swz(sK + hoff, krow + l32, 16 * (s & 3) + 8 * g);
+          const u32x4_t av = lds_load16_swz(sV + hoff, krow + l32, 16 * (s & 3) + 8 * g);
+          sacc = E::mfma(ak, qf[s], sacc);
+          pacc = E::mfma(av, df[s], pacc);
         }
-      } else {
+        // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.
+        if ((causal && kb0 + 31 > qw0) || kb0 + 32 > T) {
+          // Diagonal block or sequence tail: zero P where the key is after the
+          // query or past the end.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pacc[r] *= fast_exp2(fmaf(sacc[r], scale_log2, -L2));
-      }
-      const u32x4_t ds0 = pack_operand_e<E>(pacc, 0), ds1 = pack_operand_e<E>(pacc, 8);
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const float p = fast_exp2(fmaf(sacc[r], scale_log2, -L2));
+            pacc[r] *= ((causal && key > my_q) || key >= T) ? 0.f : p;
+          }
+        } else {
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const uint16_t* sKh = sK + (db >> 1) * (HALF_BYTES / 2);
-        dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, 32 * kh, 32 * (db & 1), lane), ds0, dq_acc[db]);
-        dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, 32 * kh + 16, 32 * (db & 1), lane), ds1, dq_acc[db]);
+          for (int r = 0; r < 16; ++r) pacc[r] *= fast_exp2(fmaf(sacc[r], scale_log2, -L2));
+        }
+        const u32x4_t ds0 = pack_operand_e<E>(pacc, 0), ds1 = pack_operand_e<E>(pacc, 8);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const uint16_t* sKh = sK + (db >> 1) * (HALF_BYTES / 2);
+          dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, krow, 32 * (db & 1), lane), ds0, dq_acc[db]);
+          dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, krow + 16, 32 * (db & 1), lane), ds1, dq_acc[db]);
+        }
       }
     }
     wait_loads();  // the next tile has landed in LDS

@@ -100,6 +100,37 @@ def test_outputs_are_overwritten_not_accumulated():
         assert torch.equal(t, ref[name]), name
 
 
+@pytest.mark.parametrize("name", ["gqa-4x1024", "mha-32x1024"])
+def test_every_unit_writes_its_outputs(name):
+    """Output buffers filled with NaN before the launches: every element of o,
+    lse, dq, dk, dv comes out finite and equal to a run into fresh buffers, so
+    every workgroup's unit (at these sizes the forward's paired order and the
+    co-launched backward's padding are in play) wrote its part exactly once."""
+    w = W.WORKLOADS[name]
+    inp = W.generate(w)
+    q, k, v, dO = to_device(inp)
+    say("every unit writes", w.label())
+    ref = run_gpu(inp, (q, k, v, dO))
+    lib = A.load_library()
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full((w.B, w.Hq, w.T), nan, device=q.device)
+    dq, dk, dv = torch.full_like(q, nan), torch.full_like(k, nan), torch.full_like(v, nan)
+    ws = torch.full((A.workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, A.ATTN_BF16),), 255,
+                    dtype=torch.uint8, device=q.device)
+    s = torch.cuda.current_stream().cuda_stream
+    shp = (w.B, w.T, w.Hq, w.Hkv, w.D, w.scale, int(w.causal), A.ATTN_BF16)
+    assert lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        *shp, s) == 0
+    assert lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        dO.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *shp,
+                        ws.data_ptr(), ws.numel(), s) == 0
+    torch.cuda.synchronize()
+    for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t.float()).all()), n
+        assert torch.equal(t, ref[n]), n
+
+
 def test_steps_compose_to_bwd():
     """attn_bwd == preprocess, then dkdv, then dq through the step entry points (bitwise)."""
     w = W.WORKLOADS["gqa-1x512"]
