@@ -69,6 +69,20 @@ def test_edge_case_parity(case):
     check_against(gpu, oracle_full(inp), dtype, w.label())
 
 
+@pytest.mark.parametrize("shape", [(1, 1408, 24, 8), (3, 1024, 12, 4)],
+                         ids=["paired-order-264-workgroups", "group-count-12-fallback"])
+def test_forward_unit_orders(shape):
+    """Forward grids of 257..512 workgroups: 264 with 8 KV groups (the paired
+    order, one shared CU per XCD) and 288 with 12 (not a multiple of 8: the
+    plain heaviest-first order)."""
+    B, T, Hq, Hkv = shape
+    w = W.custom(B, T, Hq, Hkv, 64, "bf16", seed=61 + T)
+    inp = W.generate(w)
+    say("forward unit order", w.label())
+    gpu = as_numpy(run_gpu(inp))
+    check_against(gpu, oracle_full(inp), "bf16", w.label())
+
+
 def test_scale_other_than_default():
     w = W.custom(1, 160, 4, 2, 64, "bf16", seed=7, scale=0.3)
     inp = W.generate(w)
