@@ -243,43 +243,94 @@ __device__ __forceinline__ void unit_body(
         Lr[4 * jj + 0] = l4.x; Lr[4 * jj + 1] = l4.y; Lr[4 * jj + 2] = l4.z; Lr[4 * jj + 3] = l4.w;
       }
       f32x16_t sacc = zero16();
+      if constexpr (Dm::KV_REGS) {
+        // 64-wide heads: the step's LDS operands are all read up front; the S
+        // chain runs first, then dP's products interleaved with the
+        // exponentials, then dV's products interleaved with dS, then dK's.
+        u32x4_t da[NQ], ta[ND][4];
 #pragma unroll
-      for (int c = 0; c < NQ; ++c) {
-        const int ho = (c >> 2) * HALF_ELEMS, col = 16 * (c & 3) + 8 * g;
-        sacc = E::mfma(lds_load16_swz(sQ + ho, l32, col), Dm::KV_REGS ? kf[c] : k_operand(c), sacc);
-        pacc = E::mfma(lds_load16_swz(sdO + ho, l32, col), Dm::KV_REGS ? vf[c] : v_operand(c), pacc);
-      }
-      // pacc now holds dP - delta.
-      if ((causal && q0 == k0) || q0 + 31 >= T) {
-        // Diagonal block or sequence tail: zero P where the key is after the
-        // query or the query row does not exist.
+        for (int c = 0; c < NQ; ++c) da[c] = lds_load16_swz(sdO, l32, 16 * c + 8 * g);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          float p = fast_exp2(fmaf(sacc[r], scale_log2, -Lr[r]));
-          p = ((causal && my_key > qi) || qi >= T) ? 0.f : p;
-          sacc[r] = p;
-          pacc[r] *= p;
+        for (int c = 0; c < NQ; ++c) sacc = E::mfma(lds_load16_swz(sQ, l32, 16 * c + 8 * g), kf[c], sacc);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          ta[db][0] = lds_operand_T_swz(sdO, 0, 32 * db, lane);
+          ta[db][1] = lds_operand_T_swz(sdO, 16, 32 * db, lane);
+          ta[db][2] = lds_operand_T_swz(sQ, 0, 32 * db, lane);
+          ta[db][3] = lds_operand_T_swz(sQ, 16, 32 * db, lane);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) pacc = E::mfma(da[c], vf[c], pacc);  // dP - delta
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], scale_log2, -Lr[r]));
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if ((causal && q0 == k0) || q0 + 31 >= T) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if ((causal && my_key > qi) || qi >= T) sacc[r] = 0.f;
+          }
+        }
+        const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          dv_acc[db] = E::mfma(ta[db][0], pb0, dv_acc[db]);
+          dv_acc[db] = E::mfma(ta[db][1], pb1, dv_acc[db]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[r] *= sacc[r];
+        const u32x4_t sb0 = pack_operand_e<E>(pacc, 0), sb1 = pack_operand_e<E>(pacc, 8);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          dk_acc[db] = E::mfma(ta[db][2], sb0, dk_acc[db]);
+          dk_acc[db] = E::mfma(ta[db][3], sb1, dk_acc[db]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);  // pack P
+#pragma unroll
+        for (int i = 0; i < 2 * ND; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // a dV product
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // dS and its packing
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * ND, 1);  // dK's products
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[r], scale_log2, -Lr[r]));
-          sacc[r] = p;
-          pacc[r] *= p;
+        for (int c = 0; c < NQ; ++c) {
+          const int ho = (c >> 2) * HALF_ELEMS, col = 16 * (c & 3) + 8 * g;
+          sacc = E::mfma(lds_load16_swz(sQ + ho, l32, col), k_operand(c), sacc);
+          pacc = E::mfma(lds_load16_swz(sdO + ho, l32, col), v_operand(c), pacc);
         }
-      }
-      const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
-      const u32x4_t sb0 = pack_operand_e<E>(pacc, 0), sb1 = pack_operand_e<E>(pacc, 8);
+        // pacc now holds dP - delta.  P = exp2(S scale log2e - lse log2e), then on
+        // the diagonal block or the sequence tail P = 0 where the key is after the
+        // query or the query row does not exist; then dS = P (dP - delta).
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const uint16_t* sdOh = sdO + (db >> 1) * HALF_ELEMS;
-        const uint16_t* sQh = sQ + (db >> 1) * HALF_ELEMS;
-        const int c0 = 32 * (db & 1);
-        dv_acc[db] = E::mfma(lds_operand_T_swz(sdOh, 0, c0, lane), pb0, dv_acc[db]);
-        dk_acc[db] = E::mfma(lds_operand_T_swz(sQh, 0, c0, lane), sb0, dk_acc[db]);
-        dv_acc[db] = E::mfma(lds_operand_T_swz(sdOh, 16, c0, lane), pb1, dv_acc[db]);
-        dk_acc[db] = E::mfma(lds_operand_T_swz(sQh, 16, c0, lane), sb1, dk_acc[db]);
+        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], scale_log2, -Lr[r]));
+        if ((causal && q0 == k0) || q0 + 31 >= T) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if ((causal && my_key > qi) || qi >= T) sacc[r] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[r] *= sacc[r];
+        const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
+        const u32x4_t sb0 = pack_operand_e<E>(pacc, 0), sb1 = pack_operand_e<E>(pacc, 8);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const uint16_t* sdOh = sdO + (db >> 1) * HALF_ELEMS;
+          const uint16_t* sQh = sQ + (db >> 1) * HALF_ELEMS;
+          const int c0 = 32 * (db & 1);
+          dv_acc[db] = E::mfma(lds_operand_T_swz(sdOh, 0, c0, lane), pb0, dv_acc[db]);
+          dk_acc[db] = E::mfma(lds_operand_T_swz(sQh, 0, c0, lane), sb0, dk_acc[db]);
+          dv_acc[db] = E::mfma(lds_operand_T_swz(sdOh, 16, c0, lane), pb1, dv_acc[db]);
+          dk_acc[db] = E::mfma(lds_operand_T_swz(sQh, 16, c0, lane), sb1, dk_acc[db]);
+        }
       }
       wave_lds_fence();  // this buffer's reads complete before it is refilled
       if (Dm::NBUF == 1 && s + gs < nsteps) issue_step(s + gs, 0, l_raw, d_raw);

@@ -161,34 +161,77 @@ __device__ __forceinline__ void unit_body(
       const bool active = kb0 < T && (!causal || kb0 <= qw0 + 31);
       if (active) {
         f32x16_t sacc = zero16(), pacc = neg_delta;  // dP^T - delta accumulates from -delta
-#pragma unroll
-        for (int s = 0; s < NQ; ++s) {  // first product adds to a literal zero
-          const int hoff = (s >> 2) * (HALF_BYTES / 2);  // elements to the 64-column half
-          const u32x4_t ak = lds_load16_swz(sK + hoff, krow + l32, 16 * (s & 3) + 8 * g);
-          const u32x4_t av = lds_load16_swz(sV + hoff, krow + l32, 16 * (s & 3) + 8 * g);
-          sacc = E::mfma(ak, qf[s], sacc);
-          pacc = E::mfma(av, df[s], pacc);
-        }
         // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.
-        if ((causal && kb0 + 31 > qw0) || kb0 + 32 > T) {
-          // Diagonal block or sequence tail: zero P where the key is after the
-          // query or past the end.
+        const bool masked = (causal && kb0 + 31 > qw0) || kb0 + 32 > T;
+        if constexpr (kD == 64) {
+          // The block's LDS operands are read up front; the S chain runs first,
+          // then dP's products interleaved with the exponentials, then the mask
+          // (diagonal block or sequence tail), dS and dQ's products.
+          u32x4_t av[NQ], at[ND][2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const float p = fast_exp2(fmaf(sacc[r], scale_log2, -L2));
-            pacc[r] *= ((causal && key > my_q) || key >= T) ? 0.f : p;
+          for (int c = 0; c < NQ; ++c) av[c] = lds_load16_swz(sV, krow + l32, 16 * c + 8 * g);
+#pragma unroll
+          for (int c = 0; c < NQ; ++c) sacc = E::mfma(lds_load16_swz(sK, krow + l32, 16 * c + 8 * g), qf[c], sacc);
+#pragma unroll
+          for (int db = 0; db < ND; ++db) {
+            at[db][0] = lds_operand_T_swz(sK, krow, 32 * db, lane);
+            at[db][1] = lds_operand_T_swz(sK, krow + 16, 32 * db, lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < NQ; ++c) pacc = E::mfma(av[c], df[c], pacc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], scale_log2, -L2));
+#pragma unroll
+          for (int i = 0; i < NQ; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+              if ((causal && key > my_q) || key >= T) sacc[r] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pacc[r] *= sacc[r];
+          const u32x4_t ds0 = pack_operand_e<E>(pacc, 0), ds1 = pack_operand_e<E>(pacc, 8);
+#pragma unroll
+          for (int db = 0; db < ND; ++db) {
+            dq_acc[db] = E::mfma(at[db][0], ds0, dq_acc[db]);
+            dq_acc[db] = E::mfma(at[db][1], ds1, dq_acc[db]);
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) pacc[r] *= fast_exp2(fmaf(sacc[r], scale_log2, -L2));
-        }
-        const u32x4_t ds0 = pack_operand_e<E>(pacc, 0), ds1 = pack_operand_e<E>(pacc, 8);
+          for (int s = 0; s < NQ; ++s) {  // first product adds to a literal zero
+            const int hoff = (s >> 2) * (HALF_BYTES / 2);  // elements to the 64-column half
+            const u32x4_t ak = lds_load16_swz(sK + hoff, krow + l32, 16 * (s & 3) + 8 * g);
+            const u32x4_t av = lds_load16_swz(sV + hoff, krow + l32, 16 * (s & 3) + 8 * g);
+            sacc = E::mfma(ak, qf[s], sacc);
+            pacc = E::mfma(av, df[s], pacc);
+          }
+          if (masked) {
+            // Diagonal block or sequence tail: zero P where the key is after the
+            // query or past the end.
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const uint16_t* sKh = sK + (db >> 1) * (HALF_BYTES / 2);
-          dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, krow, 32 * (db & 1), lane), ds0, dq_acc[db]);
-          dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, krow + 16, 32 * (db & 1), lane), ds1, dq_acc[db]);
+            for (int r = 0; r < 16; ++r) {
+              const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+              const float p = fast_exp2(fmaf(sacc[r], scale_log2, -L2));
+              pacc[r] *= ((causal && key > my_q) || key >= T) ? 0.f : p;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pacc[r] *= fast_exp2(fmaf(sacc[r], scale_log2, -L2));
+          }
+          const u32x4_t ds0 = pack_operand_e<E>(pacc, 0), ds1 = pack_operand_e<E>(pacc, 8);
+#pragma unroll
+          for (int db = 0; db < ND; ++db) {
+            const uint16_t* sKh = sK + (db >> 1) * (HALF_BYTES / 2);
+            dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, krow, 32 * (db & 1), lane), ds0, dq_acc[db]);
+            dq_acc[db] = E::mfma(lds_operand_T_swz(sKh, krow + 16, 32 * (db & 1), lane), ds1, dq_acc[db]);
+          }
         }
       }
     }
