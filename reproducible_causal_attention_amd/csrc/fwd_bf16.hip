@@ -121,15 +121,17 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
   const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
   const uint32_t ld_off = (uint32_t)ld_row * kv_row + (uint32_t)kvh * kD * 2 + 2 * ld_col;
   u32x4_t kreg[NL], vreg[NL], kc[NL], ksn[NL];
-  auto gload_tile = [&](int kt) {  // rows past the sequence end read as zero
-    const uint32_t off = ld_off + (uint32_t)(kt * BN) * kv_row;
+  // Loads of tile kt; rows past the sequence end read as zero, and with
+  // present == false every access is out of range (zeros, no memory traffic).
+  auto gload_tile = [&](int kt, bool present = true) {
+    const uint32_t off = present ? ld_off + (uint32_t)(kt * BN) * kv_row : 0x80000000u;
 #pragma unroll
     for (int c = 0; c < NL; ++c) {
       kreg[c] = bload16(rk, off + 128 * c);
       vreg[c] = bload16(rv, off + 128 * c);
     }
     if (kRope) {  // pairs ld_col/2 + 32c + 0..3 of key row kt*BN + ld_row
-      const uint32_t toff = ((uint32_t)(kt * BN + ld_row) * kHalf + ld_col / 2) * 4;
+      const uint32_t toff = present ? ((uint32_t)(kt * BN + ld_row) * kHalf + ld_col / 2) * 4 : 0x80000000u;
 #pragma unroll
       for (int c = 0; c < NL; ++c) {
         kc[c] = bload16(rtc, toff + 128 * c);
@@ -175,7 +177,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
 
   for (int kt = 0; kt < n_kv; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < n_kv) gload_tile(kt + 1);  // next tile's loads overlap this tile's math
+    // The next tile's loads overlap this tile's math; after the last tile they are
+    // empty and its store fills the unused buffer with zeros, so neither needs a
+    // branch that would split the loop body's scheduling regions.
+    gload_tile(kt + 1, kt + 1 < n_kv);
     const uint16_t* sK = smem + (2 * cur) * TILE;
     const uint16_t* sV = smem + (2 * cur + 1) * TILE;
     const int kb0 = kt * BN + 32 * kh;
@@ -241,8 +246,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
         oacc[db] = E::mfma(lds_operand_T(sV, PITCH, 32 * kh, 32 * db, lane), pb0, oacc[db]);
         oacc[db] = E::mfma(lds_operand_T(sV, PITCH, 32 * kh + 16, 32 * db, lane), pb1, oacc[db]);
       }
+      store_tile(cur ^ 1);
+    } else {
+      store_tile(cur ^ 1);
     }
-    if (kt + 1 < n_kv) store_tile(cur ^ 1);
     __syncthreads();
   }
 
