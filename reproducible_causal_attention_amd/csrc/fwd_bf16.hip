@@ -11,10 +11,13 @@
 // Decomposition (MI355X-first, not the page's Ampere design):
 //   * a workgroup of 8 waves owns 128 query rows of one (batch, query head):
 //     four 32-row query blocks times two key halves;
-//   * key/value tiles of 64 rows are staged row-major in LDS (pitch 72 bf16, so
-//     16-byte column reads of 32 consecutive rows hit distinct banks) and
-//     double-buffered; wave (qb, kh) runs an online softmax over keys
-//     32*kh .. 32*kh+31 of every tile, so each K/V row in LDS feeds four waves;
+//   * key/value tiles of 64 rows (128 for 64-wide heads when the grid fits the
+//     GPU in one round: half the barriers) are staged row-major in LDS (pitch
+//     72 bf16, so 16-byte column reads of 32 consecutive rows hit distinct
+//     banks) and double-buffered; wave (qb, kh) runs an online softmax over the
+//     32-key blocks kh, kh + 2, kh + 4, ... (keys 64j + 32kh .. +31 of each
+//     64-key half of a tile), so each K/V row in LDS feeds four waves and the
+//     tile size does not change the result;
 //   * the wave computes S^T = K Q^T (keys x queries) with 32x32x16 bf16 MFMA, so
 //     every lane holds one query's scores: the row max and row sum need a single
 //     half-wave exchange (v_permlane32_swap), and O^T += V^T P^T takes the
@@ -37,14 +40,15 @@ namespace rca {
 namespace {
 
 constexpr int BM = 128;    // query rows per workgroup
-constexpr int BN = 64;     // key rows per LDS tile
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
 constexpr float kSlack = 8.0f;   // lazy-rescale threshold, base-2 units
 
 // Head-dimension dependent sizes (kD = 64 or 128).
-template <int kD>
+template <int kD, int kBN>
 struct Dims {
+  static constexpr int BN = kBN;                 // key rows per LDS tile (64 or 128)
+  static constexpr int NB = BN / 64;             // 32-key blocks per wave per tile
   static constexpr int PITCH = kD + 8;           // LDS row pitch in elements (144 / 272 bytes)
   static constexpr int TILE = BN * PITCH;        // one K or V tile
   static constexpr int PART_STRIDE = kD / 2 + 4;  // floats per lane in the merge buffer (O, m, l)
@@ -56,13 +60,19 @@ struct Dims {
 
 // kRope: q and k are rotated as they are loaded (rotary tables rcos, rsin:
 // [T, kD/2] float32, pair i of position t at t*kD/2 + i), v is not.
-template <bool kPosScale, class E, bool kRope, int kD>
+// kBN: key rows per LDS tile.  With 128 each wave takes two 32-key blocks of a
+// tile (the same blocks in the same order as with 64, so the same bits) and
+// meets half the barriers; it pays off where a grid fits the GPU in one round,
+// and is used there for 64-wide heads without rotary positions (whose second
+// row of tables would cost the second workgroup per CU).
+template <bool kPosScale, class E, bool kRope, int kD, int kBN>
 __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ o,
     float* __restrict__ lse, int B, int T, int Hq, int Hkv, float scale_log2, int causal) {
-  using Dm = Dims<kD>;
+  using Dm = Dims<kD, kBN>;
   constexpr int PITCH = Dm::PITCH, TILE = Dm::TILE, NQ = Dm::NQ, ND = Dm::ND, NL = Dm::NL;
+  constexpr int BN = Dm::BN, NB = Dm::NB;
   constexpr uint32_t kHalf = kD / 2;  // rotary pairs per row
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // [buffer][K, V]
 
@@ -117,38 +127,48 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
       qsn[s] = bload16(rts, ((uint32_t)my_q * kHalf + 8 * s + 4 * g) * 4);
     }
   }
-  // Tile loads: thread -> row ld_row, columns ld_col + 64c + 0..7 for c < NL.
+  // Tile loads: thread -> rows ld_row + 64rr for rr < NB, columns ld_col + 64c + 0..7
+  // for c < NL.
   const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
   const uint32_t ld_off = (uint32_t)ld_row * kv_row + (uint32_t)kvh * kD * 2 + 2 * ld_col;
-  u32x4_t kreg[NL], vreg[NL], kc[NL], ksn[NL];
+  u32x4_t kreg[NB][NL], vreg[NB][NL], kc[NB][NL], ksn[NB][NL];
   // Loads of tile kt; rows past the sequence end read as zero, and with
   // present == false every access is out of range (zeros, no memory traffic).
   auto gload_tile = [&](int kt, bool present = true) {
-    const uint32_t off = present ? ld_off + (uint32_t)(kt * BN) * kv_row : 0x80000000u;
 #pragma unroll
-    for (int c = 0; c < NL; ++c) {
-      kreg[c] = bload16(rk, off + 128 * c);
-      vreg[c] = bload16(rv, off + 128 * c);
-    }
-    if (kRope) {  // pairs ld_col/2 + 32c + 0..3 of key row kt*BN + ld_row
-      const uint32_t toff = present ? ((uint32_t)(kt * BN + ld_row) * kHalf + ld_col / 2) * 4 : 0x80000000u;
+    for (int rr = 0; rr < NB; ++rr) {
+      const uint32_t off = present ? ld_off + (uint32_t)(kt * BN + 64 * rr) * kv_row : 0x80000000u;
 #pragma unroll
       for (int c = 0; c < NL; ++c) {
-        kc[c] = bload16(rtc, toff + 128 * c);
-        ksn[c] = bload16(rts, toff + 128 * c);
+        kreg[rr][c] = bload16(rk, off + 128 * c);
+        vreg[rr][c] = bload16(rv, off + 128 * c);
+      }
+      if (kRope) {  // pairs ld_col/2 + 32c + 0..3 of key row kt*BN + 64rr + ld_row
+        const uint32_t toff =
+            present ? ((uint32_t)(kt * BN + 64 * rr + ld_row) * kHalf + ld_col / 2) * 4 : 0x80000000u;
+#pragma unroll
+        for (int c = 0; c < NL; ++c) {
+          kc[rr][c] = bload16(rtc, toff + 128 * c);
+          ksn[rr][c] = bload16(rts, toff + 128 * c);
+        }
       }
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < NL; ++c) {
-      if (kRope) {
+    for (int rr = 0; rr < NB; ++rr) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          kreg[c][e] = rope_rotate<E>(kreg[c][e], bits_to_float(kc[c][e]), bits_to_float(ksn[c][e]));
+      for (int c = 0; c < NL; ++c) {
+        if (kRope) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            kreg[rr][c][e] = rope_rotate<E>(kreg[rr][c][e], bits_to_float(kc[rr][c][e]),
+                                            bits_to_float(ksn[rr][c][e]));
+        }
+        const int at = (ld_row + 64 * rr) * PITCH + ld_col + 64 * c;
+        lds_store16(smem + (2 * buf) * TILE + at, kreg[rr][c]);
+        lds_store16(smem + (2 * buf + 1) * TILE + at, vreg[rr][c]);
       }
-      lds_store16(smem + (2 * buf) * TILE + ld_row * PITCH + ld_col + 64 * c, kreg[c]);
-      lds_store16(smem + (2 * buf + 1) * TILE + ld_row * PITCH + ld_col + 64 * c, vreg[c]);
     }
   };
 
@@ -183,73 +203,77 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
     gload_tile(kt + 1, kt + 1 < n_kv);
     const uint16_t* sK = smem + (2 * cur) * TILE;
     const uint16_t* sV = smem + (2 * cur + 1) * TILE;
-    const int kb0 = kt * BN + 32 * kh;
-    const bool active = kb0 < T && (!causal || kb0 <= qw0 + 31);
-    if (active) {
-      f32x16_t sacc = zero16();
+    // Wave kh takes keys 64sb + 32kh .. +31 of the tile, so over the tiles it
+    // visits the 32-key blocks kh, kh + 2, kh + 4, ... in order.
 #pragma unroll
-      for (int s = 0; s < NQ; ++s)
-        sacc = E::mfma(lds_load16(sK + (32 * kh + l32) * PITCH + 16 * s + 8 * g), qf[s], sacc);
-      // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.  The
-      // tile maximum is taken over the raw scores (the scale is positive; for a
-      // negative scale the minimum) and scaled once.
-      const bool edge = (causal && kb0 + 31 > qw0) || kb0 + 32 > T;
-      bool keep[16];
-      float mraw;
-      if (edge) {
-        // Diagonal tile or sequence tail: keys after the query or past the end
-        // take no part in the maximum and get probability 0.
-        mraw = kPosScale ? -__builtin_inff() : __builtin_inff();
+    for (int sb = 0; sb < NB; ++sb) {
+      const int krow = 64 * sb + 32 * kh;  // first tile row of this 32-key block
+      const int kb0 = kt * BN + krow;
+      const bool active = kb0 < T && (!causal || kb0 <= qw0 + 31);
+      if (active) {
+        f32x16_t sacc = zero16();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          keep[r] = !((causal && key > my_q) || key >= T);
-          const float x = keep[r] ? sacc[r] : (kPosScale ? -__builtin_inff() : __builtin_inff());
-          mraw = kPosScale ? fmaxf(mraw, x) : fminf(mraw, x);
+        for (int s = 0; s < NQ; ++s)
+          sacc = E::mfma(lds_load16(sK + (krow + l32) * PITCH + 16 * s + 8 * g), qf[s], sacc);
+        // Register r holds key kb0 + 8*(r/4) + 4g + r%4 against query my_q.  The
+        // tile maximum is taken over the raw scores (the scale is positive; for a
+        // negative scale the minimum) and scaled once.
+        const bool edge = (causal && kb0 + 31 > qw0) || kb0 + 32 > T;
+        bool keep[16];
+        float mraw;
+        if (edge) {
+          // Diagonal tile or sequence tail: keys after the query or past the end
+          // take no part in the maximum and get probability 0.
+          mraw = kPosScale ? -__builtin_inff() : __builtin_inff();
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            keep[r] = !((causal && key > my_q) || key >= T);
+            const float x = keep[r] ? sacc[r] : (kPosScale ? -__builtin_inff() : __builtin_inff());
+            mraw = kPosScale ? fmaxf(mraw, x) : fminf(mraw, x);
+          }
+        } else {
+          mraw = sacc[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mraw = kPosScale ? fmaxf(mraw, sacc[r]) : fminf(mraw, sacc[r]);
         }
-      } else {
-        mraw = sacc[0];
+        const float mx = halves_max(mraw * scale_log2);
+        // Lazy rescale: the running max only moves when some row's maximum grew by
+        // more than kSlack (base-2 units), so probabilities stay below 2^kSlack
+        // (exact in bf16 and fp32) and O is rescaled a few times per row, not per tile.
+        const float m_cand = fmaxf(m_run, mx);
+        if (__any(m_cand > m_run + kSlack)) {
+          const float alpha = fast_exp2(m_run - m_cand);
+          l_run *= alpha;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mraw = kPosScale ? fmaxf(mraw, sacc[r]) : fminf(mraw, sacc[r]);
-      }
-      const float mx = halves_max(mraw * scale_log2);
-      // Lazy rescale: the running max only moves when some row's maximum grew by
-      // more than kSlack (base-2 units), so probabilities stay below 2^kSlack
-      // (exact in bf16 and fp32) and O is rescaled a few times per row, not per tile.
-      const float m_cand = fmaxf(m_run, mx);
-      if (__any(m_cand > m_run + kSlack)) {
-        const float alpha = fast_exp2(m_run - m_cand);
-        l_run *= alpha;
+          for (int db = 0; db < ND; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          }
+          m_run = m_cand;
+        }
+        if (edge) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(sacc[r], scale_log2, -m_run));
+            sacc[r] = keep[r] ? p : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], scale_log2, -m_run));
+        }
+        const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
+        // Row sum of the bf16 probabilities that enter O (two per v_dot2c_f32_bf16).
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l_run = E::add_pair(pb1[i], E::add_pair(pb0[i], l_run));
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          oacc[db] = E::mfma(lds_operand_T(sV, PITCH, krow, 32 * db, lane), pb0, oacc[db]);
+          oacc[db] = E::mfma(lds_operand_T(sV, PITCH, krow + 16, 32 * db, lane), pb1, oacc[db]);
         }
-        m_run = m_cand;
       }
-      if (edge) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[r], scale_log2, -m_run));
-          sacc[r] = keep[r] ? p : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(fmaf(sacc[r], scale_log2, -m_run));
-      }
-      const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
-      // Row sum of the bf16 probabilities that enter O (two per v_dot2c_f32_bf16).
-#pragma unroll
-      for (int i = 0; i < 4; ++i) l_run = E::add_pair(pb1[i], E::add_pair(pb0[i], l_run));
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        oacc[db] = E::mfma(lds_operand_T(sV, PITCH, 32 * kh, 32 * db, lane), pb0, oacc[db]);
-        oacc[db] = E::mfma(lds_operand_T(sV, PITCH, 32 * kh + 16, 32 * db, lane), pb1, oacc[db]);
-      }
-      store_tile(cur ^ 1);
-    } else {
-      store_tile(cur ^ 1);
     }
+    store_tile(cur ^ 1);
     __syncthreads();
   }
 
@@ -295,7 +319,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
 }  // namespace
 
 const char* fwd_bf16_tiles() {
-  return "fwd_bf16{BM=128,BN=64,waves=8(4 query x 2 key),mfma=32x32x16,D=64|128}";
+  return "fwd_bf16{BM=128,BN=64|128(d64 grids<=512),waves=8(4 query x 2 key),mfma=32x32x16,D=64|128}";
 }
 
 template <class E, bool kRope>
@@ -303,11 +327,15 @@ hipError_t launch_fwd_e(const Problem& p, const void* q, const void* k, const vo
                         const float* rcos, const float* rsin, void* o, float* lse, hipStream_t s) {
   const int n_qt = (p.T + BM - 1) / BM;
   const dim3 grid((unsigned)(n_qt * p.B * p.Hq));
-  auto kernel = p.D == 128
-                    ? (p.scale_log2 >= 0.f ? attn_fwd_kernel<true, E, kRope, 128>
-                                           : attn_fwd_kernel<false, E, kRope, 128>)
-                    : (p.scale_log2 >= 0.f ? attn_fwd_kernel<true, E, kRope, 64>
-                                           : attn_fwd_kernel<false, E, kRope, 64>);
+  const bool pos = p.scale_log2 >= 0.f;
+  auto kernel = p.D == 128 ? (pos ? attn_fwd_kernel<true, E, kRope, 128, 64>
+                                  : attn_fwd_kernel<false, E, kRope, 128, 64>)
+                           : (pos ? attn_fwd_kernel<true, E, kRope, 64, 64>
+                                  : attn_fwd_kernel<false, E, kRope, 64, 64>);
+  if constexpr (!kRope) {
+    if (p.D == 64 && grid.x <= 512)  // the grid fits the GPU in one round
+      kernel = pos ? attn_fwd_kernel<true, E, false, 64, 128> : attn_fwd_kernel<false, E, false, 64, 128>;
+  }
   kernel<<<grid, NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), rcos, rsin, static_cast<uint16_t*>(o), lse, p.B, p.T, p.Hq,
