@@ -11,7 +11,7 @@
 // Decomposition (MI355X-first, not the page's Ampere design):
 //   * a workgroup of 8 waves owns 128 query rows of one (batch, query head):
 //     four 32-row query blocks times two key halves;
-//   * key/value tiles of 64 rows (128 for 64-wide heads when the grid fits the
+//   * key/value tiles of 64 rows (128 when the grid fits the
 //     GPU in one round: half the barriers) are staged row-major in LDS (pitch
 //     72 bf16, so 16-byte column reads of 32 consecutive rows hit distinct
 //     banks) and double-buffered; wave (qb, kh) runs an online softmax over the
@@ -62,9 +62,9 @@ struct Dims {
 // [T, kD/2] float32, pair i of position t at t*kD/2 + i), v is not.
 // kBN: key rows per LDS tile.  With 128 each wave takes two 32-key blocks of a
 // tile (the same blocks in the same order as with 64, so the same bits) and
-// meets half the barriers; it pays off where a grid fits the GPU in one round,
-// and is used there for 64-wide heads without rotary positions (whose second
-// row of tables would cost the second workgroup per CU).
+// meets half the barriers; it pays off where a grid fits the GPU in one round
+// and is used there without rotary positions (whose second row of tables would
+// cost the second 64-wide workgroup per CU).
 template <bool kPosScale, class E, bool kRope, int kD, int kBN>
 __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(
 }  // namespace
 
 const char* fwd_bf16_tiles() {
-  return "fwd_bf16{BM=128,BN=64|128(d64 grids<=512),waves=8(4 query x 2 key),mfma=32x32x16,D=64|128}";
+  return "fwd_bf16{BM=128,BN=64|128(grids<=512),waves=8(4 query x 2 key),mfma=32x32x16,D=64|128}";
 }
 
 template <class E, bool kRope>
@@ -335,6 +335,8 @@ hipError_t launch_fwd_e(const Problem& p, const void* q, const void* k, const vo
   if constexpr (!kRope) {
     if (p.D == 64 && grid.x <= 512)  // the grid fits the GPU in one round
       kernel = pos ? attn_fwd_kernel<true, E, false, 64, 128> : attn_fwd_kernel<false, E, false, 64, 128>;
+    if (p.D == 128 && grid.x <= 512)
+      kernel = pos ? attn_fwd_kernel<true, E, false, 128, 128> : attn_fwd_kernel<false, E, false, 128, 128>;
   }
   kernel<<<grid, NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
