@@ -107,6 +107,24 @@ def test_batch_invariance():
         assert torch.equal(one["lse"][0], full["lse"][b]), (b, "lse")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_tile_size_does_not_change_bits(D):
+    """The forward picks 128-key tiles for grids of at most 512 workgroups and
+    64-key tiles above: a batch of 8 at T = 1024 (768 workgroups, 64-key
+    tiles) and its elements computed alone (96 workgroups, 128-key tiles)
+    give the same bits, as both visit a row's 32-key blocks in the same order."""
+    w = W.custom(8, 1024, 12, 4, D, "bf16", seed=24, scale=D ** -0.5)
+    inp = W.generate(w)
+    q, k, v, _ = to_device(inp)
+    say("tile-size invariance", w.label())
+    o_full, lse_full = A.fwd(q, k, v, w.scale, True)
+    for b in (0, 7):
+        o_one, lse_one = A.fwd(*(t[b:b + 1].contiguous() for t in (q, k, v)), w.scale, True)
+        torch.cuda.synchronize()
+        assert torch.equal(o_one[0], o_full[b]), b
+        assert torch.equal(lse_one[0], lse_full[b]), b
+
+
 def test_kv_group_invariance():
     """One KV-head group computed alone equals its slice of the GQA call, bitwise
     (the head-parallel split of a sharded run)."""
