@@ -172,3 +172,76 @@ def ref_bwd_group(q, k, v, dO, scale, causal, b, g):
     dOs = dO[b:b + 1, :, g * G:(g + 1) * G]
     dq, dk, dv, delta = ref_bwd(qs, ks, vs, dOs, scale, causal)
     return dq[0], dk[0, :, 0], dv[0, :, 0], delta[0]
+
+
+def _row_stats(q, k, v, dO, scale, causal, b, h, i):
+    """One query row of head ``h``: the definitions above for row ``i`` alone.
+
+    Returns ``(p, o_i, lse_i, delta_i, ds, n)``: the probabilities and dS of the
+    row over its ``n`` visible keys (``i + 1`` under the causal mask, else T).
+    Cost O(T * D), so long sequences can be checked row by row.
+    """
+    Hq, Hkv, T = q.shape[2], k.shape[2], q.shape[1]
+    g = kv_head_of(h, Hq, Hkv)
+    n = i + 1 if causal else T
+    kh = np.asarray(k[b, :n, g], dtype=np.float64)
+    vh = np.asarray(v[b, :n, g], dtype=np.float64)
+    qi = np.asarray(q[b, i, h], dtype=np.float64)
+    dOi = np.asarray(dO[b, i, h], dtype=np.float64) if dO is not None else None
+    s = scale * (kh @ qi)
+    m = s.max()
+    lse = m + np.log(np.exp(s - m).sum())
+    p = np.exp(s - lse)
+    o = p @ vh
+    if dOi is None:
+        return p, o, lse, None, None, n
+    delta = float(dOi @ o)
+    ds = p * (vh @ dOi - delta)
+    return p, o, lse, delta, ds, n
+
+
+def ref_query_rows(q, k, v, dO, scale, causal, b, h, rows):
+    """o, lse, delta and dq of the listed query rows of (batch ``b``, head ``h``).
+
+    Same definitions as :func:`ref_fwd` and :func:`ref_bwd`, evaluated one row
+    at a time (a row of causal attention needs only its own query and the keys
+    it sees), so the cost is O(len(rows) * T * D) instead of O(T^2 * D).
+    Returns a dict of float64 arrays: ``o`` and ``dq`` [len(rows), D], ``lse``
+    and ``delta`` [len(rows)].
+    """
+    D = q.shape[3]
+    out = {"o": np.empty((len(rows), D)), "lse": np.empty(len(rows)),
+           "delta": np.empty(len(rows)), "dq": np.empty((len(rows), D))}
+    g = kv_head_of(h, q.shape[2], k.shape[2])
+    for r, i in enumerate(rows):
+        _, o, lse, delta, ds, n = _row_stats(q, k, v, dO, scale, causal, b, h, i)
+        out["o"][r], out["lse"][r], out["delta"][r] = o, lse, delta
+        out["dq"][r] = scale * (ds @ np.asarray(k[b, :n, g], dtype=np.float64))
+    return out
+
+
+def ref_key_rows(q, k, v, dO, scale, causal, b, g, keys):
+    """dk and dv of the listed key rows of (batch ``b``, KV head ``g``).
+
+    dk_j and dv_j sum over every query row that sees key j (rows i >= j under
+    the causal mask, else all rows) of every query head of the group; each such
+    row's probabilities come from its own full row (:func:`_row_stats`).  The
+    cost is O(rows seen * T * D), small for keys near the end of a causal
+    sequence.  Returns ``(dk, dv)`` as float64 [len(keys), D].
+    """
+    T, Hq, Hkv, D = q.shape[1], q.shape[2], k.shape[2], q.shape[3]
+    G = Hq // Hkv
+    keys = list(keys)
+    first = min(keys) if causal else 0
+    dk = np.zeros((len(keys), D))
+    dv = np.zeros((len(keys), D))
+    for h in range(g * G, (g + 1) * G):
+        for i in range(first, T):
+            p, _, _, _, ds, n = _row_stats(q, k, v, dO, scale, causal, b, h, i)
+            qi = np.asarray(q[b, i, h], dtype=np.float64)
+            dOi = np.asarray(dO[b, i, h], dtype=np.float64)
+            for r, j in enumerate(keys):
+                if j < n:  # key j is visible to row i
+                    dk[r] += scale * ds[j] * qi
+                    dv[r] += p[j] * dOi
+    return dk, dv

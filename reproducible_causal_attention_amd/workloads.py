@@ -28,8 +28,9 @@ at the pages' shapes:
 * ``gqa-4x1024-d128`` -- the headline shape with 128-wide heads (scale 1/sqrt(128)).
 
 Generation recipe: ``numpy.random.Generator(PCG64(seed))``; ``standard_normal``
-in float64 drawn in the order Q, K, V, dO, each in C order of its
-[B, T, H, D] shape; Q multiplied by ``q_std``; cast to float32; for bf16
+in float64 (in float32 for workloads marked ``draw_f32``, a faster draw used
+for test shapes of half a billion elements) drawn in the order Q, K, V, dO,
+each in C order of its [B, T, H, D] shape; Q multiplied by ``q_std``; cast to float32; for bf16
 workloads rounded to bfloat16 with round-to-nearest-even (float16 workloads:
 numpy's float32 -> float16 conversion, also round-to-nearest-even).  The oracle
 sees the stored values widened exactly to float64.
@@ -55,6 +56,7 @@ class Workload:
     scale: float = 0.125
     causal: bool = True
     description: str = ""
+    draw_f32: bool = False  # draw in float32 (faster; used by the largest test shapes)
 
     @property
     def G(self) -> int:
@@ -111,8 +113,9 @@ WORKLOADS = {
 
 
 def custom(B, T, Hq, Hkv, D=64, dtype="bf16", seed=0, q_std=1.0, scale=0.125,
-           causal=True, name="custom") -> Workload:
-    return Workload(name, B, T, Hq, Hkv, D, dtype, seed, q_std, scale, causal)
+           causal=True, name="custom", draw_f32=False) -> Workload:
+    return Workload(name, B, T, Hq, Hkv, D, dtype, seed, q_std, scale, causal,
+                    draw_f32=draw_f32)
 
 
 def rope_tables(T: int, D: int, base: float = 10000.0):
@@ -173,7 +176,7 @@ def generate(w: Workload) -> Inputs:
     kshape = (w.B, w.T, w.Hkv, w.D)
     out = {}
     for name, shape in (("q", qshape), ("k", kshape), ("v", kshape), ("dO", qshape)):
-        a = rng.standard_normal(shape)
+        a = rng.standard_normal(shape, dtype=np.float32 if w.draw_f32 else np.float64)
         if name == "q" and w.q_std != 1.0:
             a *= w.q_std
         a = a.astype(np.float32)
