@@ -110,7 +110,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one MI355X: the attention path has no cross-GPU step and "
-              "this build runs on a single GPU; run with --gpus 1.", file=sys.stderr)
+              "the benchmark runs on a single GPU; run with --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np

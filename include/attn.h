@@ -192,9 +192,9 @@ attn_status_t attn_bwd_rope(const void* q, const void* k, const void* v, const v
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status_t status);
 
-/* Static string describing this build: source revision, offload architecture,
- * compiler and tile constants.  Output bits are promised identical only
- * between runs of the same build ("rust-trainer", section "Build once, run
+/* Static string describing the compiled library: source revision, offload
+ * architecture, compiler and tile constants.  Output bits are promised
+ * identical only between runs of the same compiled library ("rust-trainer", section "Build once, run
  * many", prints the resolved revision of every binary it measures). */
 const char* attn_build_info(void);
 
