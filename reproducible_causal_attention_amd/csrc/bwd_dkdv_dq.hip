@@ -1,13 +1,14 @@
 // bwd_dkdv_dq.hip -- dK/dV (a3) and dQ (a4) co-launched in one grid.
 //
 // After the preprocess the two backward kernels are independent, so one grid
-// runs the units of both: first the dQ units, heaviest query tiles first, then
-// the dK/dV units.  Under the causal mask the dQ units vary in length while the
-// dK/dV units (pairs of key blocks) are all equal; a CU that finishes a short
-// dQ tile takes a dK/dV unit next instead of idling until a separate dK/dV
-// launch, which matters when the grids are only a few units per CU.  Every
-// unit computes exactly what it computes in its own kernel (same code, same
-// order), so the results are bitwise those of the two separate launches.
+// runs the units of both.  Under the causal mask the dQ units vary in length
+// while the dK/dV units (pairs of key blocks) are all equal; a fixed number of
+// workgroups, one per CU, each run a balanced list of units (dQ tiles paired
+// heavy with light, then dK/dV units), so that no CU idles until a separate
+// dK/dV launch and the last units do not start late on CUs that drew long
+// ones.  Every unit computes exactly what it computes in its own kernel (same
+// code, same order), so the results are bitwise those of the two separate
+// launches.
 #include "dkdv_body.hpp"
 #include "dq_body.hpp"
 
@@ -15,10 +16,6 @@ namespace rca {
 namespace {
 
 constexpr int kThreads = dkdv::NTHREADS;
-// Unit order of the grid: the dQ units heaviest first, then the dK/dV units (all
-// of equal length under the causal pairing); or, with kDkdvFirst, the dK/dV
-// units first (the longest-first order, measured 1 us slower at 4 x 1024).
-constexpr bool kDkdvFirst = false;
 static_assert(dqb::NTHREADS == kThreads, "both bodies run 512-thread workgroups");
 template <int kD>
 constexpr int smem_bytes() {
@@ -26,36 +23,36 @@ constexpr int smem_bytes() {
                                                                 : dqb::Dims<kD>::SMEM_BYTES;
 }
 
-// Workgroup i < n_first runs unit i of the first kind; n_first <= i < second_base
-// exit at once (padding, so that every unit of the second kind keeps the XCD,
-// i % 8, it has in its own grid); then unit i - second_base of the second kind.
-// kRope: q and k are the rotated q', k' and dq, dk are mapped back through the
-// rotations in the epilogues (tables rcos, rsin).
+// Persistent order: P workgroups (a multiple of 8, at most one per CU; workgroup
+// w runs on XCD w % 8 like unit w of a plain grid).  Workgroup w = 8l + x takes,
+// among the units u = x + 8m of its XCD, first the dQ units in boustrophedon
+// order over m (m = l, 2Q-1-l, 2Q+l, 4Q-1-l, ... with Q = P / 8, so a heavy
+// query tile is paired with a light one), then the dK/dV units m = Q-1-l,
+// 2Q-1-l, ... (from the other end, so that when there are fewer units than
+// workgroups the two kinds land on different workgroups).  Every unit is taken
+// exactly once, and each computes exactly what it computes in its own kernel,
+// so the results do not depend on P.
 template <class E, bool kRope, int kD>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dq,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
-    float scale, float scale_log2, int causal, int n_dq, int n_kv, int second_base) {
+    float scale, float scale_log2, int causal, int n_dq, int n_kv, int P) {
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<kD>()];
-  const int i = blockIdx.x;
-  if (kDkdvFirst) {
-    if (i < n_kv) {
-      dkdv::unit_body<E, kRope, kD>(smem, i, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T, Hq,
-                                    Hkv, scale, scale_log2, causal);
-    } else if (i >= second_base) {
-      dqb::unit_body<E, kRope, kD>(smem, i - second_base, q, k, v, dO, lse, delta, rcos, rsin, dq,
-                                   B, T, Hq, Hkv, scale, scale_log2, causal);
-    }
-  } else {
-    if (i < n_dq) {
-      dqb::unit_body<E, kRope, kD>(smem, i, q, k, v, dO, lse, delta, rcos, rsin, dq, B, T, Hq, Hkv,
-                                   scale, scale_log2, causal);
-    } else if (i >= second_base) {
-      dkdv::unit_body<E, kRope, kD>(smem, i - second_base, q, k, v, dO, lse, delta, rcos, rsin, dk,
-                                    dv, B, T, Hq, Hkv, scale, scale_log2, causal);
-    }
+  const int x = blockIdx.x & 7, l = blockIdx.x >> 3, Q = P >> 3;
+  for (int j = 0;; ++j) {
+    const int m = 2 * Q * (j >> 1) + ((j & 1) ? 2 * Q - 1 - l : l);
+    const int u = x + 8 * m;
+    if (u >= n_dq) break;  // m grows with j
+    dqb::unit_body<E, kRope, kD>(smem, u, q, k, v, dO, lse, delta, rcos, rsin, dq, B, T, Hq, Hkv,
+                                 scale, scale_log2, causal);
+    __syncthreads();  // the next unit reuses the LDS
+  }
+  for (int u = x + 8 * (Q - 1 - l); u < n_kv; u += 8 * Q) {
+    dkdv::unit_body<E, kRope, kD>(smem, u, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T, Hq,
+                                  Hkv, scale, scale_log2, causal);
+    __syncthreads();
   }
 }
 
@@ -69,17 +66,20 @@ hipError_t launch_bwd_dkdv_dq_e(const Problem& p, const void* q, const void* k, 
   const int n_dq = ((p.T + dqb::BM - 1) / dqb::BM) * p.B * p.Hq;
   const int nkb = (p.T + 31) / 32;
   const int n_kv = (nkb + 1) / 2 * p.B * p.Hkv;
-  // The second kind's units start at a multiple of 8, so each keeps the XCD
-  // (block % 8) it has in its own grid.
-  const int n_first = kDkdvFirst ? n_kv : n_dq;
-  const int second_base = (n_first + 7) / 8 * 8;
-  const dim3 grid((unsigned)(second_base + (kDkdvFirst ? n_dq : n_kv)));
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipGetLastError();
+  // One workgroup per CU (the body's registers and LDS allow no more), or one
+  // per unit with a margin of two per XCD when the units are fewer.
+  const int units = n_dq + n_kv + 16;
+  const int P = ((n_cu < units ? n_cu : units) + 7) / 8 * 8;
   auto kernel = p.D == 128 ? attn_bwd_dkdv_dq_kernel<E, kRope, 128> : attn_bwd_dkdv_dq_kernel<E, kRope, 64>;
-  kernel<<<grid, kThreads, 0, s>>>(
+  kernel<<<dim3((unsigned)P), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta, rcos, rsin,
       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), p.B,
-      p.T, p.Hq, p.Hkv, p.scale, p.scale_log2, p.causal, n_dq, n_kv, second_base);
+      p.T, p.Hq, p.Hkv, p.scale, p.scale_log2, p.causal, n_dq, n_kv, P);
   return hipGetLastError();
 }
 

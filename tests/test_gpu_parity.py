@@ -119,7 +119,8 @@ def test_every_unit_writes_its_outputs(name):
     """Output buffers filled with NaN before the launches: every element of o,
     lse, dq, dk, dv comes out finite and equal to a run into fresh buffers, so
     every workgroup's unit (at these sizes the forward's paired order and the
-    co-launched backward's padding are in play) wrote its part exactly once."""
+    co-launched backward's per-workgroup unit lists are in play) wrote its part
+    exactly once."""
     w = W.WORKLOADS[name]
     inp = W.generate(w)
     q, k, v, dO = to_device(inp)
@@ -178,7 +179,7 @@ def test_colaunched_backward_equals_two_launches(name):
 
 @pytest.mark.parametrize("shape", [(3, 333, 6, 2), (1, 65, 12, 4), (2, 200, 4, 4)])
 def test_colaunched_backward_odd_grids(shape):
-    """Odd unit counts: the dQ part not a multiple of 8 (padding workgroups), odd
+    """Odd unit counts: the dQ part not a multiple of 8 (XCD lists of different lengths), odd
     key-block counts (a middle block), non-causal."""
     B, T, Hq, Hkv = shape
     w = W.custom(B, T, Hq, Hkv, 64, "bf16", seed=41 + T)
