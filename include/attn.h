@@ -140,11 +140,12 @@ attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const voi
                           attn_dtype_t dtype, void* stream);
 
 /* Backward steps 2 and 3 co-launched in one grid (they are independent once
- * delta is known): the dQ units of attn_bwd_dq, heaviest first, then the dK/dV
- * units of attn_bwd_dkdv, so a CU that finishes a short dQ tile takes dK/dV work
- * instead of waiting for a second launch.  dq, dk and dv are bitwise those of
- * the two separate calls.  Arguments as there; dq, dk, dv must not overlap any
- * input or each other. */
+ * delta is known): one workgroup per CU runs a fixed list of the dQ units of
+ * attn_bwd_dq (heavy query tiles paired with light ones) and then dK/dV units
+ * of attn_bwd_dkdv, so no CU waits for a second launch.  dq, dk and dv are
+ * bitwise those of the two separate calls, whatever the CU count.  Arguments
+ * as there; dq, dk, dv must not overlap any input or each other.  Queries the
+ * current device's CU count (hipDeviceGetAttribute) to size the grid. */
 attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dO,
                                const float* lse, const float* delta, void* dq, void* dk, void* dv,
                                int B, int T, int Hq, int Hkv, int D, float scale, int causal,
