@@ -11,12 +11,16 @@ transformer in pure Rust: RustingBrain vs PyTorch and TensorFlow" (section
 "The setup": GQA 12/4, head_dim 64) at the 4 x 1024 batch shape.
 
 Timing protocol: the correctness gate runs first (finite outputs, bitwise-equal
-hashes over repeated runs, exact-math invariants of the gradients), then
-``--warmup`` untimed steps, then each kernel alone (back-to-back launches between
-two HIP events) to find the dominant one, then exactly ``--steps`` steps between
+hashes over repeated runs, exact-math invariants of the gradients), then each
+kernel alone (back-to-back launches between two HIP events) to find the
+dominant one, then ``--warmup`` untimed steps right before the timed region (the
+step time falls by a few percent over the first ~10 ms of continuous load as
+the GPU's clocks settle, so the default warmup covers 18 ms), then exactly ``--steps`` steps between
 two device synchronisations, with HIP events around the dominant kernel in every
 8th step, so its average duration inside the steps gives the roofline figure
-without serialising the other launches (an event pair costs its step ~2 us).  ``value`` is algorithmic
+without serialising the other launches (an event pair costs its step ~2 us);
+then 5 trials of 10 steps, each between two HIP events, for the spread
+(``trials``: per-trial us per step, mean, min, max).  ``value`` is algorithmic
 TFLOP/s (4*D forward + 10*D backward flops per unmasked (query, key) pair and
 query head) over the wall-clock time of the timed steps, inputs resident in HBM.
 
@@ -86,8 +90,8 @@ def load_traffic(kernel: str, workload: str, digest: str):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="gqa-4x1024")
     ap.add_argument("--layers", type=int, default=16,
                     help="also time a stack of this many independent layers (0: skip)")
@@ -264,10 +268,6 @@ def main() -> int:
         print(json.dumps({"metric": "gate failed", "gate": gate}), flush=True)
         return 1
 
-    for _ in range(args.warmup):
-        step((q, k, v, dO), bufs)
-    torch.cuda.synchronize()
-
     # ---- per-kernel durations: back-to-back launches of one kernel, GPU events ----
     # (picks the dominant kernel; the timed region below re-measures that one in place)
     per_kernel_us = {}
@@ -285,6 +285,10 @@ def main() -> int:
         torch.cuda.synchronize()
         per_kernel_us[n] = 1e3 * e0.elapsed_time(e1) / n_rep
     dom = max(names, key=per_kernel_us.get)
+
+    for _ in range(args.warmup):
+        step((q, k, v, dO), bufs)
+    torch.cuda.synchronize()
 
     # ---- timed region: whole steps; the dominant kernel is bracketed by events in
     # every 8th step (each event pair adds ~2 us to its step) ----
@@ -309,6 +313,23 @@ def main() -> int:
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     log(f"step {ms_per_step * 1e3:.1f} us wall, {event_step_us:.1f} us by events; "
         f"{tflops:.1f} TFLOP/s; kernels alone {per_kernel_us}; {dom} in the steps {dom_us:.2f} us")
+
+    # ---- spread: 5 trials of 10 steps each, HIP events around each trial (after
+    # the timed region; reported beside `value`, which the region above gives) ----
+    trial_us = []
+    for _ in range(5):
+        et = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        et[0].record(stream)
+        for _ in range(10):
+            step((q, k, v, dO), bufs)
+        et[1].record(stream)
+        torch.cuda.synchronize()
+        trial_us.append(1e3 * et[0].elapsed_time(et[1]) / 10)
+    trials = {"trials": 5, "steps_each": 10, "us_per_step": [round(t, 2) for t in trial_us],
+              "mean": round(float(np.mean(trial_us)), 2), "min": round(min(trial_us), 2),
+              "max": round(max(trial_us), 2)}
+    log(f"trials (5 x 10 steps) us per step: {trials['us_per_step']}")
 
     # ---- roofline of the dominant kernel ----
     pairs = w.causal_pairs
@@ -412,6 +433,7 @@ def main() -> int:
         "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "per_kernel_us": {n: round(u, 2) for n, u in per_kernel_us.items()},
         "event_step_us": round(event_step_us, 2),
+        "trials": trials,
         "preprocess_gbs": round(pre_gbs, 1) if pre_gbs is not None else None,
         "roofline": roof,
         "cpu_baseline": cpu,

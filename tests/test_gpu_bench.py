@@ -34,3 +34,6 @@ def test_bench_json_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     assert d["gate"]["ok"]
+    tr = d["trials"]
+    assert tr["trials"] == 5 and len(tr["us_per_step"]) == 5
+    assert tr["min"] <= tr["mean"] <= tr["max"] and tr["min"] > 0
