@@ -5,9 +5,12 @@ kernels of the library.  torch supplies device memory (``torch.empty``) and the
 stream (``torch.cuda.current_stream()``).  If the library is missing the calls
 raise; there is no fallback.
 
-Layouts: q, o, dO, dq are [B, T, Hq, 64]; k, v, dk, dv are [B, T, Hkv, 64]
-(contiguous, bfloat16, float16 or float32); lse and delta are [B, Hq, T] float32.
-The rotary variants take cos and sin tables [T, 32] float32 (bf16 / fp16 only).
+Layouts: q, o, dO, dq are [B, T, Hq, D]; k, v, dk, dv are [B, T, Hkv, D]
+(contiguous, one dtype: bfloat16, float16 or float32; D = 64, or 128 for the
+16-bit types); lse and delta are [B, Hq, T] float32.  The rotary variants take
+cos and sin tables [T, D/2] float32 (bf16 / fp16 only).  Every wrapper checks
+the shapes, dtypes and device of all its tensors against q before it hands a
+pointer to the library, which sizes every buffer from q's shape.
 """
 from __future__ import annotations
 
@@ -110,12 +113,61 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _shapes(q, k):
+def _shapes(q, k, v=None, *, o=None, dO=None, lse=None, delta=None):
+    """(B, T, Hq, Hkv, D) from q and k, after checking every given tensor against them.
+
+    The C ABI sizes every buffer from these five numbers, so a tensor of another
+    shape, dtype or device would be read or written out of its bounds: raise
+    ValueError instead.  q, k, v, o, dO share q's dtype and device; k and v are
+    [B, T, Hkv, D]; o and dO are q's shape; lse and delta are [B, Hq, T] float32.
+    """
+    if not isinstance(q, torch.Tensor) or not isinstance(k, torch.Tensor):
+        raise ValueError("q and k must be torch tensors")
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B, T, Hq, D] and k, v [B, T, Hkv, D]")
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
+    kv_shape = (B, T, Hkv, D)
+    checks = [("k", k, kv_shape)]
+    if v is not None:
+        checks.append(("v", v, kv_shape))
+    for name, t in (("o", o), ("dO", dO)):
+        if t is not None:
+            checks.append((name, t, tuple(q.shape)))
+    for name, t, shape in checks:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} is {t.dtype} but q is {q.dtype}: all inputs share one dtype")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device} but q is on {q.device}")
+    for name, t in (("lse", lse), ("delta", delta)):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if tuple(t.shape) != (B, Hq, T) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 of shape {(B, Hq, T)}, "
+                             f"got {t.dtype} {tuple(t.shape)}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device} but q is on {q.device}")
     return B, T, Hq, Hkv, D
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _workspace(workspace, nbytes: int, device):
+    """The caller's workspace (any dtype, sized in bytes; the library checks the
+    size), or a new one of ``nbytes`` bytes on ``device``."""
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+        raise ValueError(f"workspace must be a tensor on {device}")
+    return workspace
 
 
 def default_scale(D: int) -> float:
@@ -124,8 +176,8 @@ def default_scale(D: int) -> float:
 
 def fwd(q, k, v, scale=None, causal=True):
     """Forward: returns ``(o [B,T,Hq,D], lse [B,Hq,T] float32)``."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
     lib = load_library()
-    B, T, Hq, Hkv, D = _shapes(q, k)
     scale = default_scale(D) if scale is None else float(scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
@@ -140,23 +192,25 @@ def workspace_bytes(B, T, Hq, Hkv, D, dtype_code) -> int:
 
 def bwd(q, k, v, o, lse, dO, scale=None, causal=True, workspace=None):
     """Backward of sum(o * dO): returns ``(dq, dk, dv)``."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v, o=o, dO=dO, lse=lse)
     lib = load_library()
-    B, T, Hq, Hkv, D = _shapes(q, k)
     scale = default_scale(D) if scale is None else float(scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nbytes = workspace_bytes(B, T, Hq, Hkv, D, _dtype_code(q))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
                         _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale, int(bool(causal)),
-                        _dtype_code(q), _ptr(workspace), workspace.numel(), _stream()))
+                        _dtype_code(q), _ptr(workspace), _nbytes(workspace), _stream()))
     return dq, dk, dv
 
 
 def bwd_preprocess(o, dO):
     """delta = rowsum(dO * o) as [B, Hq, T] float32."""
-    lib = load_library()
+    if not isinstance(o, torch.Tensor) or o.dim() != 4:
+        raise ValueError("o must be [B, T, Hq, D]")
+    _shapes(o, o, o, dO=dO)
     B, T, Hq, D = o.shape
+    lib = load_library()
     delta = torch.empty((B, Hq, T), dtype=torch.float32, device=o.device)
     _check(lib.attn_bwd_preprocess(_ptr(o), _ptr(dO), _ptr(delta), B, T, Hq, D,
                                    _dtype_code(o), _stream()))
@@ -164,8 +218,8 @@ def bwd_preprocess(o, dO):
 
 
 def bwd_dkdv(q, k, v, dO, lse, delta, scale=None, causal=True):
+    B, T, Hq, Hkv, D = _shapes(q, k, v, dO=dO, lse=lse, delta=delta)
     lib = load_library()
-    B, T, Hq, Hkv, D = _shapes(q, k)
     scale = default_scale(D) if scale is None else float(scale)
     dk, dv = torch.empty_like(k), torch.empty_like(v)
     _check(lib.attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
@@ -175,8 +229,8 @@ def bwd_dkdv(q, k, v, dO, lse, delta, scale=None, causal=True):
 
 
 def bwd_dq(q, k, v, dO, lse, delta, scale=None, causal=True):
+    B, T, Hq, Hkv, D = _shapes(q, k, v, dO=dO, lse=lse, delta=delta)
     lib = load_library()
-    B, T, Hq, Hkv, D = _shapes(q, k)
     scale = default_scale(D) if scale is None else float(scale)
     dq = torch.empty_like(q)
     _check(lib.attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
@@ -188,8 +242,8 @@ def bwd_dq(q, k, v, dO, lse, delta, scale=None, causal=True):
 def bwd_dkdv_dq(q, k, v, dO, lse, delta, scale=None, causal=True):
     """dK/dV and dQ co-launched in one grid: returns ``(dq, dk, dv)``, bitwise those
     of ``bwd_dkdv`` and ``bwd_dq``."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v, dO=dO, lse=lse, delta=delta)
     lib = load_library()
-    B, T, Hq, Hkv, D = _shapes(q, k)
     scale = default_scale(D) if scale is None else float(scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     _check(lib.attn_bwd_dkdv_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
@@ -200,7 +254,7 @@ def bwd_dkdv_dq(q, k, v, dO, lse, delta, scale=None, causal=True):
 
 def _tables(cos, sin, T, D):
     for t in (cos, sin):
-        if t.dtype != torch.float32 or tuple(t.shape) != (T, D // 2):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or tuple(t.shape) != (T, D // 2):
             raise ValueError(f"rotary tables must be float32 [T, D/2] = [{T}, {D // 2}]")
     return _ptr(cos), _ptr(sin)
 
@@ -208,8 +262,8 @@ def _tables(cos, sin, T, D):
 def fwd_rope(q, k, v, cos, sin, scale=None, causal=True):
     """Forward with rotary embedding of q and k (adjacent pairs, tables [T, D/2]):
     returns ``(o, lse)``."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
     lib = load_library()
-    B, T, Hq, Hkv, D = _shapes(q, k)
     scale = default_scale(D) if scale is None else float(scale)
     pc, ps = _tables(cos, sin, T, D)
     o = torch.empty_like(q)
@@ -225,16 +279,15 @@ def rope_workspace_bytes(B, T, Hq, Hkv, D, dtype_code) -> int:
 
 def bwd_rope(q, k, v, o, lse, dO, cos, sin, scale=None, causal=True, workspace=None):
     """Backward of ``fwd_rope``: ``(dq, dk, dv)`` with respect to the unrotated q, k, v."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v, o=o, dO=dO, lse=lse)
     lib = load_library()
-    B, T, Hq, Hkv, D = _shapes(q, k)
     scale = default_scale(D) if scale is None else float(scale)
     pc, ps = _tables(cos, sin, T, D)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nbytes = rope_workspace_bytes(B, T, Hq, Hkv, D, _dtype_code(q))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
     _check(lib.attn_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), pc, ps,
                              _ptr(dq), _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale,
-                             int(bool(causal)), _dtype_code(q), _ptr(workspace), workspace.numel(),
+                             int(bool(causal)), _dtype_code(q), _ptr(workspace), _nbytes(workspace),
                              _stream()))
     return dq, dk, dv
