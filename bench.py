@@ -87,14 +87,145 @@ def load_traffic(kernel: str, workload: str, digest: str):
     return rec.get("bytes_per_launch")
 
 
+def load_kernel_time(kernel: str, workload: str, digest: str):
+    """Average rocprofv3 duration (us) of one launch of ``kernel`` on ``workload`` from
+    the committed kernel-trace summaries, if taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload, {}).get(kernel)
+    if not rec or rec.get("sources_digest") != digest:
+        return None
+    return rec.get("avg_us")
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics (shader) clock through amdsmi from a host
+    thread while the GPU runs; reports the median of the samples in MHz, or None
+    where amdsmi is unavailable."""
+
+    def __init__(self, period_s: float = 0.004):
+        import threading
+        self.period_s, self.samples, self._stop = period_s, [], threading.Event()
+        self._thread, self._handle, self._amdsmi = None, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if handles:
+                self._amdsmi, self._handle = amdsmi, handles[0]
+                self._read()
+        except Exception as e:  # amdsmi missing, no permission, or no device
+            log("clock sampling unavailable:", repr(e)[:120])
+            self._amdsmi = None
+
+    def _read(self):
+        info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        import threading
+        if self._amdsmi is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        """Median, min and max over the second half of the samples (the reading lags
+        the load by tens of milliseconds)."""
+        if not self.samples:
+            return None
+        import statistics
+        late = self.samples[len(self.samples) // 2:]
+        return {"median_mhz": statistics.median(late), "min_mhz": min(late),
+                "max_mhz": max(late), "samples": len(late),
+                "source": "amdsmi GFX clock, sampled every ~4 ms while the step runs back "
+                          "to back for --clock-seconds after the timed region (second half "
+                          "of the samples)"}
+
+
+def summarize_rocprof(stats_csv: str, workload: str, command: str, digest: str | None) -> int:
+    """Write profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace --stats
+    kernel_stats.csv and record the hot-path kernels' average durations, with the
+    digest of the kernel sources they ran (the profiled bench line's
+    ``sources_digest``; default: the current tree's), in profiles/kernel_times.json."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    digest = digest or kernel_sources_digest()
+    names = {"attn_fwd_kernel": "fwd", "attn_bwd_pre_kernel": "bwd_preprocess",
+             "attn_bwd_dkdv_dq_kernel": "bwd_dkdv_dq", "attn_bwd_dkdv_kernel": "bwd_dkdv",
+             "attn_bwd_dq_kernel": "bwd_dq", "attn_bwd_rope_prep_kernel": "bwd_rope_prep"}
+    lines = [f"# rocprofv3 kernel statistics: {workload}", "",
+             "Command (from the repository root on one MI355X; TMPDIR=/tmp):", "", "```",
+             command, "```", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    times = {}
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].replace("void ", "").replace("rca::(anonymous namespace)::", "")
+        name = name.replace("rca::", "").replace("(anonymous namespace)::", "")
+        avg, mn, mx = (float(r[c]) / 1e3 for c in ("AverageNs", "MinNs", "MaxNs"))
+        share = 100.0 * float(r["TotalDurationNs"]) / total
+        if share < 0.05:
+            continue
+        lines.append(f"| {name[:72]} | {r['Calls']} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {share:.1f}% |")
+        for prefix, key in names.items():
+            if name.startswith(prefix + "<") and key not in times:
+                times[key] = {"avg_us": round(avg, 3), "calls": int(r["Calls"]), "kernel": name,
+                              "sources_digest": digest}
+    lines += ["", f"Kernel sources digest: `{digest}` (bench.py's `sources_digest`)."]
+    out_md = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        data = {"_note": "average rocprofv3 kernel-trace durations per launch, by workload and "
+                         "kernel, with the digest of the kernel sources they were taken on"}
+    data[workload] = times
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    log(f"wrote {out_md} and {path} ({len(times)} hot-path kernels)")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="gqa-4x1024")
-    ap.add_argument("--layers", type=int, default=16,
-                    help="also time a stack of this many independent layers (0: skip)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="also time a stack of this many independent layers (0: skip; "
+                         "default 16 for gqa-4x1024, else 0)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle cpu_baseline sample (0: skip)")
     ap.add_argument("--kernel-only", default=None,
@@ -102,6 +233,8 @@ def main() -> int:
                              "fwd_rope", "bwd_rope"),
                     help="counter runs: launch only this kernel --launches times and exit")
     ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--clock-seconds", type=float, default=1.0,
+                    help="seconds of back-to-back steps during which the GPU clock is sampled")
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused baseline (libattn_unfused.so) instead")
     ap.add_argument("--rope", action="store_true",
@@ -109,7 +242,19 @@ def main() -> int:
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="counter calibration: copy this many bytes device to device "
                          "--launches times and exit")
+    ap.add_argument("--summarize-rocprof", default=None, metavar="KERNEL_STATS_CSV",
+                    help="write profiles/kernels_<workload>.md and profiles/kernel_times.json "
+                         "from a rocprofv3 --stats kernel_stats.csv, then exit")
+    ap.add_argument("--command", default="",
+                    help="with --summarize-rocprof: the profiled command, quoted in the summary")
+    ap.add_argument("--sources-digest", default=None,
+                    help="with --summarize-rocprof: sources_digest of the profiled run")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        return summarize_rocprof(args.summarize_rocprof, args.workload, args.command,
+                                 args.sources_digest)
+    if args.layers is None:
+        args.layers = 16 if args.workload == "gqa-4x1024" else 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -326,6 +471,15 @@ def main() -> int:
         et[1].record(stream)
         torch.cuda.synchronize()
         trial_us.append(1e3 * et[0].elapsed_time(et[1]) / 10)
+    # ---- observed shader clock: the driver's GFX clock reading is refreshed too slowly
+    # for a timed region of tens of milliseconds, so it is sampled while the same steps
+    # run back to back for about a second (after the trials; not timed) ----
+    with ClockSampler() as clock:
+        t_end = time.perf_counter() + args.clock_seconds
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                step((q, k, v, dO), bufs)
+            torch.cuda.synchronize()
     trials = {"trials": 5, "steps_each": 10, "us_per_step": [round(t, 2) for t in trial_us],
               "mean": round(float(np.mean(trial_us)), 2), "min": round(min(trial_us), 2),
               "max": round(max(trial_us), 2)}
@@ -356,6 +510,28 @@ def main() -> int:
     roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(dom_us, 2)
+    roof["timing"] = ("frac from HIP events around the kernel inside the timed steps "
+                      "(includes one dispatch latency per launch)")
+    prof_us = load_kernel_time(dom, w.name + ("+rope" if rope else ""), src_digest)
+    if prof_us:
+        prof_sec = prof_us * 1e-6
+        if dom == "bwd_preprocess":
+            prof_ach = algo[dom] / prof_sec / 1e9
+            roof["frac_rocprof"] = round(prof_ach / PEAK_HBM_GBS, 4)
+        else:
+            prof_ach = algo[dom] / prof_sec / 1e12
+            roof["frac_rocprof"] = round(prof_ach / PEAK_BF16_TFLOPS, 4)
+        roof["rocprof_avg_us"] = prof_us
+        roof["achieved_rocprof"] = round(prof_ach, 1)
+    else:
+        roof["frac_rocprof"] = None
+    roof["per_kernel_frac_rocprof"] = {}
+    for kname in ("fwd", "bwd_dkdv_dq", "bwd_preprocess"):
+        kus = load_kernel_time(kname, w.name, src_digest) if not rope else None
+        if kus:
+            peak = PEAK_HBM_GBS if kname == "bwd_preprocess" else PEAK_BF16_TFLOPS
+            scale_ = 1e9 if kname == "bwd_preprocess" else 1e12
+            roof["per_kernel_frac_rocprof"][kname] = round(algo[kname] / (kus * 1e-6) / scale_ / peak, 4)
     if dom in ("bwd_dkdv_dq", "bwd_rope"):  # matrix work the split design executes (S and dP twice)
         roof["executed_tflops"] = round(14.0 * D * pairs / sec / 1e12, 1)
     if dom == "bwd_rope":
@@ -372,7 +548,9 @@ def main() -> int:
                torch.randn_like(k, dtype=torch.float32).to(tdt),
                torch.randn_like(v, dtype=torch.float32).to(tdt),
                torch.randn_like(dO, dtype=torch.float32).to(tdt)) for _ in range(L)]
-        bs = [buffers() for _ in range(L)]
+        ws_bytes_stack = int(lib.attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, bf))
+        bs = [dict(buffers(), ws=torch.empty(ws_bytes_stack, dtype=torch.uint8, device=dev))
+              for _ in range(L)]
 
         def stack_step():
             for i in range(L):
@@ -382,15 +560,12 @@ def main() -> int:
                        causal, bf, s)
             for i in reversed(range(L)):
                 x, b = xs[i], bs[i]
-                launch("attn_bwd_preprocess", b["o"].data_ptr(), x[3].data_ptr(),
-                       b["delta"].data_ptr(), B, T, Hq, D, bf, s)
-                launch("attn_bwd_dkdv", x[0].data_ptr(), x[1].data_ptr(), x[2].data_ptr(),
-                       x[3].data_ptr(), b["lse"].data_ptr(), b["delta"].data_ptr(),
-                       b["dk"].data_ptr(), b["dv"].data_ptr(), B, T, Hq, Hkv, D, w.scale,
-                       causal, bf, s)
-                launch("attn_bwd_dq", x[0].data_ptr(), x[1].data_ptr(), x[2].data_ptr(),
-                       x[3].data_ptr(), b["lse"].data_ptr(), b["delta"].data_ptr(),
-                       b["dq"].data_ptr(), B, T, Hq, Hkv, D, w.scale, causal, bf, s)
+                # attn_bwd itself: the preprocess into the workspace (this layer's
+                # delta buffer), then the co-launched dK/dV + dQ grid
+                launch("attn_bwd", x[0].data_ptr(), x[1].data_ptr(), x[2].data_ptr(),
+                       b["o"].data_ptr(), b["lse"].data_ptr(), x[3].data_ptr(),
+                       b["dq"].data_ptr(), b["dk"].data_ptr(), b["dv"].data_ptr(), B, T, Hq,
+                       Hkv, D, w.scale, causal, bf, b["ws"].data_ptr(), b["ws"].numel(), s)
 
         for _ in range(3):
             stack_step()
@@ -434,6 +609,10 @@ def main() -> int:
         "per_kernel_us": {n: round(u, 2) for n, u in per_kernel_us.items()},
         "event_step_us": round(event_step_us, 2),
         "trials": trials,
+        "clock": clock.summary(),
+        "pct_peak_at_observed_clock": (
+            round(100 * tflops / (PEAK_BF16_TFLOPS * clock.summary()["median_mhz"] / 2400.0), 2)
+            if clock.summary() else None),
         "preprocess_gbs": round(pre_gbs, 1) if pre_gbs is not None else None,
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -667,7 +846,7 @@ def cpu_baseline(w, inp, bufs, budget_s, tables=None):
     pairs_per_unit = G * (w.T * (w.T + 1) // 2 if w.causal else w.T * w.T)
     flops = done * pairs_per_unit * (4.0 + 10.0) * w.D
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{done} unit computations ({passes} pass{'es' if passes > 1 else ''} over the "
                       f"{len(units)} (batch, KV-group) units of {w.name}"
                       f"{' with rotary positions' if tables is not None else ''}), fwd+bwd, "

@@ -100,11 +100,20 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        attn_dtype_t dtype, void* stream);
 
 /* Bytes of device workspace attn_bwd needs: the float32 delta rows
- * (B*Hq*T*4 bytes) rounded up to 256 bytes.  Returns 0 for invalid sizes. */
+ * (B*Hq*T*4 bytes) rounded up to 256 bytes.  Returns 0 for invalid sizes.
+ * delta is the per-row term of the softmax backward; the unfused chain of
+ * "Training a 100M transformer in pure Rust: RustingBrain vs PyTorch and
+ * TensorFlow", section "Step 1: measure before changing anything", forms it
+ * inside causal_softmax_bwd, the fused backward of section "Step 2: fused flash
+ * attention" keeps it in this buffer between its steps. */
 size_t attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D, attn_dtype_t dtype);
 
-/* Backward of sum(o * dO).  o and lse must be the outputs of attn_fwd for the
- * same q, k, v, scale and causal.  Enqueues, in order, attn_bwd_preprocess
+/* Backward of sum(o * dO): the fused flash-attention backward of "Training a
+ * 100M transformer in pure Rust: RustingBrain vs PyTorch and TensorFlow",
+ * section "Step 2: fused flash attention" (dq, dk, dv as defined above, with P
+ * recomputed from lse as that page's causal_probs_from_lse does, section "Step
+ * 1: measure before changing anything").  o and lse must be the outputs of
+ * attn_fwd for the same q, k, v, scale and causal.  Enqueues, in order, attn_bwd_preprocess
  * (delta into the workspace) and attn_bwd_dkdv_dq; the results are bitwise those
  * of attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq called in turn.  dq, dk,
  * dv must not overlap any input, the workspace or each other; the workspace must
@@ -123,24 +132,37 @@ attn_status_t attn_bwd_preprocess(const void* o, const void* dO, float* delta,
                                   int B, int T, int Hq, int D, attn_dtype_t dtype,
                                   void* stream);
 
-/* Backward step 2: dk and dv.  One workgroup owns a tile of keys of one KV head
- * and visits every query head of its group and every query tile that can see
- * those keys, in a fixed order, so dk and dv are summed in registers and written
- * once, with no atomics.  delta is the output of attn_bwd_preprocess. */
+/* Backward step 2: dk and dv (definitions above): the flash_attention_dkv
+ * kernel of "Training a 100M transformer in pure Rust: RustingBrain vs PyTorch
+ * and TensorFlow", section "Where the time goes now".  One workgroup owns a
+ * tile of keys of one KV head and visits every query head of its group and
+ * every query tile that can see those keys, in a fixed order, so dk and dv are
+ * summed in registers and written once, with no atomics ("rust-trainer",
+ * section "The trainer is not bit-identical to itself after step 1", loses bit
+ * identity to an atomically accumulated gradient).  delta is the output of
+ * attn_bwd_preprocess. */
 attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
                             const float* lse, const float* delta, void* dk, void* dv,
                             int B, int T, int Hq, int Hkv, int D, float scale, int causal,
                             attn_dtype_t dtype, void* stream);
 
-/* Backward step 3: dq.  One workgroup owns a tile of queries of one query head
- * and visits the key tiles it can see in a fixed order. */
+/* Backward step 3: dq = scale * sum_j dS[i][j] k[j] (definitions above), the
+ * query-side half of the fused backward of "Training a 100M transformer in pure
+ * Rust: RustingBrain vs PyTorch and TensorFlow", section "Step 2: fused flash
+ * attention".  One workgroup owns a tile of queries of one query head and
+ * visits the key tiles it can see in a fixed order; each dq row has one owner,
+ * so there are no atomics. */
 attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                           const float* lse, const float* delta, void* dq,
                           int B, int T, int Hq, int Hkv, int D, float scale, int causal,
                           attn_dtype_t dtype, void* stream);
 
 /* Backward steps 2 and 3 co-launched in one grid (they are independent once
- * delta is known): one workgroup per CU runs a fixed list of the dQ units of
+ * delta is known; "Training a 100M transformer in pure Rust: RustingBrain vs
+ * PyTorch and TensorFlow", section "Where the time goes now", names the dk/dv
+ * kernel as the remaining attention hot spot, and the page's section "The
+ * result" notes that per-step overheads weigh more at small batches): one
+ * workgroup per CU runs a fixed list of the dQ units of
  * attn_bwd_dq (heavy query tiles paired with light ones) and then dK/dV units
  * of attn_bwd_dkdv, so no CU waits for a second launch.  dq, dk and dv are
  * bitwise those of the two separate calls, whatever the CU count.  Arguments

@@ -171,25 +171,34 @@ ATTN_EXPORT attn_status_t attn_bwd_dq(const void* q, const void* k, const void* 
                                       : rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
 }
 
-ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                                   int B, int T, int Hq, int Hkv, int D, float scale, int causal,
-                                   attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
-  ATTN_TRY(check_ptrs({q, k, v, o, lse, dO, dq, dk, dv, workspace}));
+namespace rca {
+
+// Every check of attn_bwd except those of the workspace: pointers, sizes,
+// scalars, overlap of the outputs with the inputs and each other (and with
+// [ws, ws + ws_bytes) when ws is not null), then the supported shapes.
+attn_status_t check_bwd_args(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                             int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                             attn_dtype_t dtype, const void* ws, size_t ws_bytes) {
+  ATTN_TRY(check_ptrs({q, k, v, o, lse, dO, dq, dk, dv}));
   ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
   ATTN_TRY(check_scalars(scale, causal));
-  const size_t need = attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype);
-  if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
   const size_t es = elem_size(dtype);
   const size_t qb = (size_t)B * T * Hq * D * es, kb = (size_t)B * T * Hkv * D * es;
   const size_t lb = (size_t)B * Hq * T * sizeof(float);
   ATTN_TRY(check_disjoint({span_of(q, qb), span_of(k, kb), span_of(v, kb), span_of(o, qb),
                            span_of(lse, lb), span_of(dO, qb)},
                           {span_of(dq, qb), span_of(dk, kb), span_of(dv, kb),
-                           span_of(workspace, need)}));
-  float* delta = static_cast<float*>(workspace);
-  ATTN_TRY(check_supported(D, dtype));
+                           span_of(ws, ws ? ws_bytes : 0)}));
+  return check_supported(D, dtype);
+}
+
+// The launches of attn_bwd on checked arguments: the preprocess writes delta,
+// then the co-launched dK/dV + dQ grid (float32: the two separate kernels).
+attn_status_t enqueue_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                          int T, int Hq, int Hkv, int D, float scale, int causal,
+                          attn_dtype_t dtype, float* delta, void* stream) {
   discard_stale_error();
   const rca::Problem p = make_problem(B, T, Hq, Hkv, scale, causal, D);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -204,6 +213,24 @@ ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, 
   ATTN_TRY(from_hip(rca::launch_bwd_pre_f32(p, o, dO, delta, s)));
   ATTN_TRY(from_hip(rca::launch_bwd_dkdv_f32(p, q, k, v, dO, lse, delta, dk, dv, s)));
   return from_hip(rca::launch_bwd_dq_f32(p, q, k, v, dO, lse, delta, dq, s));
+}
+
+}  // namespace rca
+
+ATTN_EXPORT attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                                   int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                                   attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  ATTN_TRY(check_ptrs({q, k, v, o, lse, dO, dq, dk, dv, workspace}));
+  ATTN_TRY(check_sizes(B, T, Hq, Hkv, D));
+  ATTN_TRY(check_scalars(scale, causal));
+  const size_t need = attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype);
+  if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
+  ATTN_TRY(rca::check_bwd_args(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, D, scale, causal,
+                               dtype, workspace, need));
+  return rca::enqueue_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, D, scale, causal, dtype,
+                          static_cast<float*>(workspace), stream);
 }
 
 ATTN_EXPORT attn_status_t attn_bwd_dkdv_dq(const void* q, const void* k, const void* v,

@@ -17,17 +17,24 @@ namespace {
 constexpr int PRE_THREADS = 256;
 constexpr int PRE_ROWS = PRE_THREADS / 8;  // 8 lanes per row, 8 elements each per 64 columns
 
-// Row of kD elements: lane `part` of the row's eight holds columns
-// 8*part + 64c + 0..7 for c < kD/64.
+// Block blk covers positions 32*tc .. 32*tc + 31 of query head h of batch element
+// b, with (b, tc, h) enumerated h fastest, so neighbouring blocks read the
+// neighbouring head segments of the same tokens and each block's 32 delta values
+// fill one 128-byte line of delta ([B, Hq, T]).  Lane `part` of a row's eight
+// holds columns 8*part + 64c + 0..7 for c < kD/64.
 template <class E, int kD>
 __device__ __forceinline__ void delta_rows(int blk, const uint16_t* __restrict__ o,
                                            const uint16_t* __restrict__ dO,
-                                           float* __restrict__ delta, int T, int Hq,
-                                           long long n_rows) {
-  const long long row = (long long)blk * PRE_ROWS + (threadIdx.x >> 3);
+                                           float* __restrict__ delta, int T, int Hq) {
+  const int n_tc = (T + PRE_ROWS - 1) / PRE_ROWS;
+  const int h = blk % Hq;
+  const int btc = blk / Hq;
+  const int b = btc / n_tc;
+  const int t = (btc - b * n_tc) * PRE_ROWS + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
+  const long long row = ((long long)b * T + t) * Hq + h;  // [b][t][h] row of o and dO
   float acc = 0.f;
-  if (row < n_rows) {
+  if (t < T) {
     u32x4_t a[kD / 64], c[kD / 64];
 #pragma unroll
     for (int ch = 0; ch < kD / 64; ++ch) {
@@ -47,26 +54,24 @@ __device__ __forceinline__ void delta_rows(int blk, const uint16_t* __restrict__
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
-  if (row < n_rows && part == 0) {
-    // row enumerates [b][t][h]; delta is [b][h][t].
-    const long long bt = row / Hq;
-    const int h = (int)(row - bt * Hq);
-    const long long b = bt / T;
-    const int t = (int)(bt - b * T);
-    delta[(b * Hq + h) * T + t] = acc;
-  }
+  if (t < T && part == 0) delta[((long long)b * Hq + h) * T + t] = acc;
+}
+
+// Blocks of the delta part of a grid: one per (batch element, 32 positions, query head).
+inline long long delta_blocks(const Problem& p) {
+  return (long long)p.B * ((p.T + PRE_ROWS - 1) / PRE_ROWS) * p.Hq;
 }
 
 template <class E, int kD>
 __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_pre_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO, float* __restrict__ delta,
-    int T, int Hq, long long n_rows) {
-  delta_rows<E, kD>(blockIdx.x, o, dO, delta, T, Hq, n_rows);
+    int T, int Hq) {
+  delta_rows<E, kD>(blockIdx.x, o, dO, delta, T, Hq);
 }
 
-// Backward preparation with rotary embedding: blocks [0, nb) write delta exactly
-// as attn_bwd_pre_kernel does, blocks [nb, 2nb) the rotated q rows and the rest
-// the rotated k rows (rope_rotate, as the forward rotates them as it loads:
+// Backward preparation with rotary embedding: blocks [0, nd) write delta exactly
+// as attn_bwd_pre_kernel does, blocks [nd, nd + nb) the rotated q rows and the
+// rest the rotated k rows (rope_rotate, as the forward rotates them as it loads:
 // the same bits), which the dK/dV and dQ kernels then read in place of q, k.
 template <class E, int kD>
 __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_rope_prep_kernel(
@@ -74,13 +79,13 @@ __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_rope_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float* __restrict__ rcos, const float* __restrict__ rsin, float* __restrict__ delta,
     uint16_t* __restrict__ q_rot, uint16_t* __restrict__ k_rot, int T, int Hq, int Hkv,
-    long long n_qrows, long long n_krows, int nb) {
+    long long n_qrows, long long n_krows, int nd, int nb) {
   int blk = blockIdx.x;
-  if (blk < nb) {
-    delta_rows<E, kD>(blk, o, dO, delta, T, Hq, n_qrows);
+  if (blk < nd) {
+    delta_rows<E, kD>(blk, o, dO, delta, T, Hq);
     return;
   }
-  blk -= nb;
+  blk -= nd;
   const uint16_t* src = q;
   uint16_t* dst = q_rot;
   int H = Hq;
@@ -116,11 +121,10 @@ __global__ __launch_bounds__(PRE_THREADS) void attn_bwd_rope_prep_kernel(
 template <class E>
 hipError_t launch_bwd_pre_e(const Problem& p, const void* o, const void* dO, float* delta,
                                hipStream_t s) {
-  const long long n_rows = (long long)p.B * p.T * p.Hq;
-  const dim3 grid((unsigned)((n_rows + PRE_ROWS - 1) / PRE_ROWS));
+  const dim3 grid((unsigned)delta_blocks(p));
   auto kernel = p.D == 128 ? attn_bwd_pre_kernel<E, 128> : attn_bwd_pre_kernel<E, 64>;
   kernel<<<grid, PRE_THREADS, 0, s>>>(static_cast<const uint16_t*>(o),
-                                      static_cast<const uint16_t*>(dO), delta, p.T, p.Hq, n_rows);
+                                      static_cast<const uint16_t*>(dO), delta, p.T, p.Hq);
   return hipGetLastError();
 }
 
@@ -129,14 +133,15 @@ hipError_t launch_bwd_rope_prep_e(const Problem& p, const void* o, const void* d
                                   const void* k, const float* rcos, const float* rsin,
                                   float* delta, void* q_rot, void* k_rot, hipStream_t s) {
   const long long n_q = (long long)p.B * p.T * p.Hq, n_k = (long long)p.B * p.T * p.Hkv;
+  const int nd = (int)delta_blocks(p);
   const int nb = (int)((n_q + PRE_ROWS - 1) / PRE_ROWS);
   const int nbk = (int)((n_k + PRE_ROWS - 1) / PRE_ROWS);
-  const dim3 grid((unsigned)(2 * nb + nbk));
+  const dim3 grid((unsigned)(nd + nb + nbk));
   auto kernel = p.D == 128 ? attn_bwd_rope_prep_kernel<E, 128> : attn_bwd_rope_prep_kernel<E, 64>;
   kernel<<<grid, PRE_THREADS, 0, s>>>(
       static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO),
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rcos, rsin, delta,
-      static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), p.T, p.Hq, p.Hkv, n_q, n_k, nb);
+      static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), p.T, p.Hq, p.Hkv, n_q, n_k, nd, nb);
   return hipGetLastError();
 }
 

@@ -5,7 +5,7 @@
 
 namespace rca {
 
-constexpr int kHeadDim = 64;
+constexpr int kHeadDim = 64;  // every dtype; the 16-bit kernels also take 128
 
 // Everything a kernel launch needs; pointers are device pointers already
 // validated by the C ABI layer (contiguous, 16-byte aligned, non-overlapping).
@@ -56,7 +56,7 @@ hipError_t launch_bwd_dq_f32(const Problem& p, const void* q, const void* k, con
                              const void* dO, const float* lse, const float* delta, void* dq,
                              hipStream_t s);
 
-// Rotary embedding (16-bit types; tables rcos, rsin: [T, 32] float32).  The
+// Rotary embedding (16-bit types; tables rcos, rsin: [T, D/2] float32).  The
 // forward rotates q and k as it loads them; the backward's preparation writes
 // delta and the rotated q', k' (q_rot, k_rot), then the co-launched dK/dV + dQ
 // grid runs on q', k' and maps dq, dk back through the rotations.

@@ -139,3 +139,57 @@ def sha256_outputs(gpu: dict) -> str:
 
 def as_numpy(gpu: dict) -> dict:
     return {n: to_f64(t) for n, t in gpu.items()}
+
+
+def unit_rows(T: int):
+    """Query rows checked in every unit: tile and block edges, the middle, the last."""
+    return sorted({r for r in (0, 31, 32, 127, 128, T // 2 + 5, T - 1) if 0 <= r < T})
+
+
+def check_every_unit(inp: W.Inputs, gpu_np: dict, where="", n_keys: int = 32):
+    """Every (batch, KV-group) unit against the row-wise oracle.
+
+    For each unit: o, lse, delta and dq of the rows of ``unit_rows`` of every
+    query head of the group (``oracle.ref_query_rows``), dk and dv of the last
+    ``n_keys`` keys of the KV head (``oracle.ref_key_rows``), each to the
+    tolerances of ``check_against`` relative to the checked rows; and the two
+    exact-math column sums over all T keys of the unit -- sum_j dv_j equals the sum
+    of dO over the group's query rows (rows of P sum to one) and sum_j dk_j = 0
+    (shifting every key by one vector leaves P unchanged) -- to the dtype's
+    tolerance relative to sum |dO| and to the largest column sum of |dk|.  A unit
+    computed for the wrong (batch, group) slot, or not at all, fails here.
+    """
+    w = inp.workload
+    q, k, v, dO = (inp.as_float64(n) for n in ("q", "k", "v", "dO"))
+    G, T = w.G, w.T
+    rows = unit_rows(T)
+    keys = list(range(max(0, T - n_keys), T))
+    tol = TOL[w.dtype]["dv"]
+    worst = {}
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            ref_u = {"o": [], "lse": [], "delta": [], "dq": []}
+            gpu_u = {"o": [], "lse": [], "delta": [], "dq": []}
+            for h in range(g * G, (g + 1) * G):
+                r = oracle.ref_query_rows(q, k, v, dO, w.scale, w.causal, b, h, rows)
+                for n in ref_u:
+                    ref_u[n].append(r[n])
+                gpu_u["o"].append(gpu_np["o"][b, rows, h])
+                gpu_u["dq"].append(gpu_np["dq"][b, rows, h])
+                gpu_u["lse"].append(gpu_np["lse"][b, h, rows])
+                gpu_u["delta"].append(gpu_np["delta"][b, h, rows])
+            ref_u = {n: np.concatenate(a) for n, a in ref_u.items()}
+            gpu_u = {n: np.concatenate(a) for n, a in gpu_u.items()}
+            ref_u["dk"], ref_u["dv"] = oracle.ref_key_rows(q, k, v, dO, w.scale, w.causal, b, g, keys)
+            gpu_u["dk"], gpu_u["dv"] = gpu_np["dk"][b, keys, g], gpu_np["dv"][b, keys, g]
+            errs = check_against(gpu_u, ref_u, w.dtype, f"{where} unit b={b} g={g}")
+            dO_g = dO[b, :, g * G:(g + 1) * G]
+            want = dO_g.sum(axis=(0, 1))
+            got = gpu_np["dv"][b, :, g].sum(axis=0)
+            errs["dv_colsum"] = float(np.max(np.abs(got - want)) / np.abs(dO_g).sum(axis=(0, 1)).max())
+            dk_u = gpu_np["dk"][b, :, g]
+            errs["dk_colsum"] = float(np.max(np.abs(dk_u.sum(axis=0))) / np.abs(dk_u).sum(axis=0).max())
+            assert errs["dv_colsum"] <= tol and errs["dk_colsum"] <= tol, (where, b, g, errs)
+            for n, e in errs.items():
+                worst[n] = max(worst.get(n, 0.0), e)
+    return worst

@@ -16,7 +16,8 @@ from reproducible_causal_attention_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["gqa-8x4096-peaked", "gqa-4x1024", "tiny-f32", "gqa-4x1024-f16"])
+@pytest.mark.parametrize("name", ["gqa-8x4096-peaked", "gqa-4x1024", "tiny-f32", "gqa-1x512",
+                                  "mha-32x1024", "gqa-4x1024-f16"])
 def test_ten_runs_identical_hashes(name):
     w = W.WORKLOADS[name]
     inp = W.generate(w)

@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_support import (as_numpy, check_against, check_units, oracle_full, run_gpu,
-                         sampled_units, say, to_device)
+from gpu_support import (as_numpy, check_against, check_every_unit, check_units, oracle_full,
+                         run_gpu, sampled_units, say, to_device)
 from reproducible_causal_attention_amd import attn as A
 from reproducible_causal_attention_amd import workloads as W
 
@@ -28,7 +28,9 @@ def test_workload_full_parity(name):
 
 @pytest.mark.parametrize("name", ["mha-32x1024", "gqa-8x4096-peaked"])
 def test_workload_sampled_parity(name):
-    """Full-size launch, checked on sampled (batch, KV-group) units."""
+    """Full-size launch: three (batch, KV-group) units against the full oracle, and
+    every unit against the row-wise oracle on fixed rows and the last keys, plus
+    its exact column sums of dk and dv."""
     w = W.WORKLOADS[name]
     inp = W.generate(w)
     say("sampled parity", name, w.label())
@@ -36,6 +38,8 @@ def test_workload_sampled_parity(name):
     for n, a in gpu.items():
         assert np.all(np.isfinite(a)), (name, n)
     print(name, check_units(inp, gpu, sampled_units(w), name))
+    say("every-unit parity", name, w.B * w.Hkv, "units")
+    print(name, "every unit:", check_every_unit(inp, gpu, name))
 
 
 EDGE_CASES = [

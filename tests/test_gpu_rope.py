@@ -148,3 +148,60 @@ def test_rope_sampled_units_at_4096():
                  "dq": gpu["dq"][b, :, hs], "dk": gpu["dk"][b, :, g], "dv": gpu["dv"][b, :, g]}
         ref_u = {"o": o_r, "lse": lse_r, "delta": dl_r, "dq": dq_r, "dk": dk_r, "dv": dv_r}
         print(check_against(gpu_u, ref_u, w.dtype, f"rope 8x4096 unit b={b} g={g}"))
+
+
+def test_rope_at_4096_against_the_unrounded_oracle():
+    """The rotary path at 8 x 4096 against the plain rotary oracle (q and k rotated
+    exactly, never rounded), with the kernel's rounding of q', k' to bf16 bounded
+    rather than handed to the oracle.
+
+    The kernel rotates each pair in float32 (two fmas: absolute error below
+    2^-22 times the pair's norm) and rounds to nearest bf16 (relative error at
+    most u = 2^-8), so each rotated element is within u a_d of the exact one,
+    a_d = |x'_d| + 2^-14 |pair|; that moves the score s_ij = scale <q'_i, k'_j>
+    by at most
+        E_ij = scale (2u + u^2) sum_d a(q'_i)_d a(k'_j)_d,
+    and the log-sum-exp of a row moves by at most the largest move of its scores,
+    so |lse_gpu - lse_exact| <= 2e-2 (the plain bf16 tolerance) + max_{j <= i} E_ij
+    row by row.  o, dq, dk, dv change with P, by a factor exp(ds - dlse) per
+    probability; the rounding errors are independent with standard deviation
+    about u / sqrt(3) of each element, so a score moves by about
+        sigma = scale (u / sqrt(3)) sqrt(2 max_ij sum_d (q'_id k'_jd)^2)
+    and these are compared at 2e-2 + 6 sigma relative to max |ref|."""
+    w = W.WORKLOADS["gqa-8x4096-peaked"]
+    inp = W.generate(w)
+    ct, st, c, s = tables(w.T)
+    say("rope vs unrounded oracle", w.label())
+    gpu = as_numpy(run_rope(w, to_device(inp), ct, st))
+    q, k, v, dO = (inp.as_float64(n) for n in ("q", "k", "v", "dO"))
+    qr, kr = oracle.apply_rope(q, c, s), oracle.apply_rope(k, c, s)  # exact, not rounded
+    u = 2.0 ** -8
+
+    def mag(x):  # a_d: |x'_d| plus 2^-14 times the norm of its rotary pair
+        pair = np.sqrt(x[..., 0::2] ** 2 + x[..., 1::2] ** 2)
+        return np.abs(x) + 2.0 ** -14 * np.repeat(pair, 2, axis=-1)
+
+    G, T = w.G, w.T
+    causal_mask = np.tril(np.ones((T, T), dtype=bool))
+    for b, g in [(0, 0), (w.B - 1, w.Hkv - 1)]:
+        o_r, lse_r = oracle.ref_fwd_group(qr, kr, v, w.scale, w.causal, b, g)
+        dq_r, dk_r, dv_r, _ = oracle.ref_bwd_group(qr, kr, v, dO, w.scale, w.causal, b, g)
+        dq_r = oracle.apply_rope_transpose(dq_r[None], c, s)[0]
+        dk_r = oracle.apply_rope_transpose(dk_r[None, :, None], c, s)[0, :, 0]
+        ka = mag(kr[b, :, g])
+        sigma = 0.0
+        for hh in range(G):
+            h = g * G + hh
+            qa = mag(qr[b, :, h])
+            E = w.scale * (2 * u + u * u) * np.where(causal_mask, qa @ ka.T, 0.0).max(axis=1)
+            err = np.abs(gpu["lse"][b, h] - lse_r[hh])
+            assert np.all(err <= 2e-2 + E), (b, h, float(err.max()), float(E.max()))
+            sq = np.where(causal_mask, (qa * qa) @ (ka * ka).T, 0.0).max()
+            sigma = max(sigma, w.scale * (u / np.sqrt(3.0)) * np.sqrt(2.0 * sq))
+        tol = 2e-2 + 6.0 * sigma
+        hs = slice(g * G, (g + 1) * G)
+        for name, a, r in (("o", gpu["o"][b, :, hs], o_r), ("dq", gpu["dq"][b, :, hs], dq_r),
+                           ("dk", gpu["dk"][b, :, g], dk_r), ("dv", gpu["dv"][b, :, g], dv_r)):
+            e = float(np.max(np.abs(a - r)) / np.max(np.abs(r)))
+            print(f"rope unrounded b={b} g={g} {name}: {e:.4g} (tolerance {tol:.4g})")
+            assert e <= tol, (b, g, name, e, tol)
