@@ -32,8 +32,10 @@
  *   lse, delta   : [B, Hq, T]     float32
  *
  * Ownership and execution.  Every pointer is caller-owned device memory on the
- * current HIP device.  The library allocates nothing, keeps no mutable global
- * state and is safe to call from several host threads.  Calls enqueue work on
+ * current HIP device.  The library allocates nothing and is safe to call from
+ * several host threads; its only global state is the per-GPU delta array of
+ * attn_bwd_noalloc (a fixed device array, not an allocation) and the cache of
+ * that array's address on each device.  Calls enqueue work on
  * `stream` (a hipStream_t; NULL is the null stream) and return without
  * waiting for it.  Outputs are overwritten, never accumulated into, so callers
  * need not clear them first.
@@ -123,6 +125,27 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int B, int T, int Hq, int Hkv, int D, float scale, int causal,
                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Size in bytes of the device array that attn_bwd_noalloc keeps per GPU for
+ * its delta rows: calls with attn_bwd_workspace_bytes() above it are refused. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+
+/* attn_bwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same checks,
+ * launches and results (bitwise those of attn_bwd), with delta kept in an array
+ * the library holds on each GPU (ATTN_NOALLOC_SCRATCH_BYTES, i.e. B*Hq*T up to
+ * 4,194,304 rows) instead of a caller workspace.  It calls no hipMalloc or
+ * hipFree.  The first call on a device resolves the array's address there
+ * (hipGetSymbolAddress); a failure is ATTN_ERR_HIP.  ATTN_ERR_INVALID_ARG, in
+ * addition to attn_bwd's cases, when attn_bwd_workspace_bytes() exceeds
+ * ATTN_NOALLOC_SCRATCH_BYTES.  All calls on one GPU share the array and its
+ * contents, so calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller; calls queued on one
+ * stream are ordered and safe. */
+attn_status_t attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                               int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                               attn_dtype_t dtype, void* stream);
 
 /* Backward step 1: delta[b][h][i] = sum_d dO[b][i][h][d] * o[b][i][h][d], accumulated
  * in float32 (the row term of the softmax backward that causal_softmax_bwd needs

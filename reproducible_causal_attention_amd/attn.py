@@ -29,7 +29,12 @@ EXPORTED = (
     "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
     "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dkdv_dq", "attn_fwd_rope",
     "attn_bwd_rope_workspace_bytes", "attn_bwd_rope", "attn_status_string", "attn_build_info",
+    "attn_bwd_noalloc",
 )
+
+# Bytes of the per-GPU array attn_bwd_noalloc keeps its delta rows in
+# (ATTN_NOALLOC_SCRATCH_BYTES in include/attn.h).
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _lib = None
 
@@ -69,8 +74,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_rope_workspace_bytes.argtypes = [*sizes, I]
     lib.attn_bwd_rope_workspace_bytes.restype = Z
     lib.attn_bwd_rope.argtypes = [P, P, P, P, P, P, P, P, P, P, P, *sizes, F, I, I, P, Z, P]
+    lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, *sizes, F, I, I, P]
     for name in ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
-                 "attn_bwd_dkdv_dq", "attn_fwd_rope", "attn_bwd_rope"):
+                 "attn_bwd_dkdv_dq", "attn_fwd_rope", "attn_bwd_rope", "attn_bwd_noalloc"):
         getattr(lib, name).restype = I
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -201,6 +207,19 @@ def bwd(q, k, v, o, lse, dO, scale=None, causal=True, workspace=None):
     _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
                         _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale, int(bool(causal)),
                         _dtype_code(q), _ptr(workspace), _nbytes(workspace), _stream()))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, dO, scale=None, causal=True):
+    """``bwd`` through attn_bwd_noalloc (delta in the library's per-GPU array, no
+    workspace): returns ``(dq, dk, dv)``, bitwise those of ``bwd``."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v, o=o, dO=dO, lse=lse)
+    lib = load_library()
+    scale = default_scale(D) if scale is None else float(scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib.attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                _ptr(dq), _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, scale,
+                                int(bool(causal)), _dtype_code(q), _stream()))
     return dq, dk, dv
 
 

@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "../../include/attn.h"
+
 namespace rca {
 
 constexpr int kHeadDim = 64;  // every dtype; the 16-bit kernels also take 128
@@ -80,6 +82,18 @@ hipError_t launch_bwd_dkdv_dq_rope_f16(const Problem& p, const void* q_rot, cons
                                        const void* v, const void* dO, const float* lse,
                                        const float* delta, const float* rcos, const float* rsin,
                                        void* dq, void* dk, void* dv, hipStream_t s);
+
+// attn_bwd in two parts (attn_api.hip): its argument checks other than the
+// workspace's (ws, if not null, must not overlap an output), and its launches
+// with delta in the given device buffer of attn_bwd_workspace_bytes() bytes.
+attn_status_t check_bwd_args(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                             int B, int T, int Hq, int Hkv, int D, float scale, int causal,
+                             attn_dtype_t dtype, const void* ws, size_t ws_bytes);
+attn_status_t enqueue_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                          int T, int Hq, int Hkv, int D, float scale, int causal,
+                          attn_dtype_t dtype, float* delta, void* stream);
 
 // Tile constants of each kernel family, reported by attn_build_info().
 const char* fwd_bf16_tiles();

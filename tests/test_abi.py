@@ -143,6 +143,48 @@ def test_bwd_validation(lib, name, over, want):
     assert bwd_call(lib, **over) == want
 
 
+def noalloc_call(lib, **over):
+    a = dict(q=BASE, k=BASE + 16 * MB, v=BASE + 32 * MB, o=BASE + 48 * MB, lse=BASE + 64 * MB,
+             dO=BASE + 80 * MB, dq=BASE + 96 * MB, dk=BASE + 112 * MB, dv=BASE + 128 * MB,
+             B=1, T=128, Hq=4, Hkv=2, D=64, scale=0.125, causal=1, dtype=A.ATTN_BF16, stream=None)
+    a.update(over)
+    return lib.attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"],
+                                a["dk"], a["dv"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+# Buffers 4 GiB apart, so that large shapes do not overlap.
+GB4 = 1 << 32
+BIG = dict(q=BASE, k=BASE + GB4, v=BASE + 2 * GB4, o=BASE + 3 * GB4, lse=BASE + 4 * GB4,
+           dO=BASE + 5 * GB4, dq=BASE + 6 * GB4, dk=BASE + 7 * GB4, dv=BASE + 8 * GB4)
+
+NOALLOC_ERRORS = [
+    ("null_dq", dict(dq=None), A.ATTN_ERR_INVALID_ARG),
+    ("dv_overlaps_o", dict(dv=BASE + 48 * MB), A.ATTN_ERR_INVALID_ARG),
+    ("groups_do_not_divide", dict(Hq=3, Hkv=2), A.ATTN_ERR_INVALID_ARG),
+    ("head_dim_32", dict(D=32), A.ATTN_ERR_UNSUPPORTED),
+    ("causal_2", dict(causal=2), A.ATTN_ERR_INVALID_ARG),
+    # delta of 2 x 4 x 2^20 rows = 32 MiB, beyond the 16 MiB scratch array
+    ("beyond_scratch", dict(BIG, B=2, T=1 << 20, Hq=4, Hkv=4), A.ATTN_ERR_INVALID_ARG),
+    ("beyond_scratch_f32", dict(BIG, B=1, T=1 << 20, Hq=5, Hkv=5, dtype=A.ATTN_F32),
+     A.ATTN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,over,want", NOALLOC_ERRORS, ids=[e[0] for e in NOALLOC_ERRORS])
+def test_bwd_noalloc_validation(lib, name, over, want):
+    """attn_bwd_noalloc applies attn_bwd's checks and the scratch size limit, all on
+    the host before any HIP call."""
+    assert noalloc_call(lib, **over) == want
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", text)
+    assert m, "ATTN_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == A.NOALLOC_SCRATCH_BYTES
+
+
 def test_step_entry_points_validate(lib):
     # preprocess: delta overlapping dO
     assert lib.attn_bwd_preprocess(BASE, BASE + 16 * MB, BASE + 16 * MB + 64, 1, 128, 4, 64,
