@@ -178,7 +178,7 @@ def summarize_rocprof(stats_csv: str, workload: str, command: str, digest: str |
     rows = list(csv.DictReader(open(stats_csv)))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     digest = digest or kernel_sources_digest()
-    names = {"attn_fwd_kernel": "fwd", "attn_bwd_pre_kernel": "bwd_preprocess",
+    names = {"attn_fwd64_kernel": "fwd", "attn_fwd_kernel": "fwd", "attn_bwd_pre_kernel": "bwd_preprocess",
              "attn_bwd_dkdv_dq_kernel": "bwd_dkdv_dq", "attn_bwd_dkdv_kernel": "bwd_dkdv",
              "attn_bwd_dq_kernel": "bwd_dq", "attn_bwd_rope_prep_kernel": "bwd_rope_prep"}
     lines = [f"# rocprofv3 kernel statistics: {workload}", "",

@@ -341,7 +341,7 @@ ATTN_EXPORT const char* attn_status_string(attn_status_t status) {
 ATTN_EXPORT const char* attn_build_info(void) {
   static const std::string info = std::string("revision=") + ATTN_GIT_REV +
                                   " arch=gfx950 compiler=clang-" + __clang_version__ + " " +
-                                  rca::fwd_bf16_tiles() + " " + rca::bwd_dkdv_tiles() + " " + rca::bwd_dq_tiles() + " " +
+                                  rca::fwd64_tiles() + " " + rca::fwd_bf16_tiles() + " " + rca::bwd_dkdv_tiles() + " " + rca::bwd_dq_tiles() + " " +
                                   rca::f32_tiles();
   return info.c_str();
 }

@@ -308,6 +308,15 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // loads in flight inside it and the compiler's waits cover just those.
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The same wait as an instruction the compiler sees (s_waitcnt vmcnt(0); the other
+// counters untouched), so its own wait-count bookkeeping knows every earlier
+// vector-memory load has completed and adds no waits for them later (an inline
+// asm wait is opaque to it: loads issued before one still count as pending).
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt = 0, expcnt = 7, lgkmcnt = 15 (gfx9 encoding)
+  asm volatile("" ::: "memory");
+}
+
 // Wait for this wave's outstanding LDS operations; also a compiler memory barrier.
 // Used between a wave's writes to its private LDS region and its own reads.
 __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

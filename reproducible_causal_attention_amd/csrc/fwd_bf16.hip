@@ -359,11 +359,13 @@ hipError_t launch_fwd_rope_f16(const Problem& p, const void* q, const void* k, c
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
                            float* lse, hipStream_t s) {
+  if (p.D == 64) return launch_fwd64_bf16(p, q, k, v, o, lse, s);
   return launch_fwd_e<Bf16, false>(p, q, k, v, nullptr, nullptr, o, lse, s);
 }
 
 hipError_t launch_fwd_f16(const Problem& p, const void* q, const void* k, const void* v, void* o,
                            float* lse, hipStream_t s) {
+  if (p.D == 64) return launch_fwd64_f16(p, q, k, v, o, lse, s);
   return launch_fwd_e<F16, false>(p, q, k, v, nullptr, nullptr, o, lse, s);
 }
 

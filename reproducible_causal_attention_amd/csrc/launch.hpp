@@ -23,6 +23,11 @@ hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const
                            float* lse, hipStream_t s);
 hipError_t launch_fwd_f16(const Problem& p, const void* q, const void* k, const void* v, void* o,
                            float* lse, hipStream_t s);
+// The 64-wide forward (fwd64.hip), used by the two above for D = 64.
+hipError_t launch_fwd64_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                             float* lse, hipStream_t s);
+hipError_t launch_fwd64_f16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                            float* lse, hipStream_t s);
 hipError_t launch_bwd_pre_bf16(const Problem& p, const void* o, const void* dO, float* delta,
                                hipStream_t s);
 hipError_t launch_bwd_pre_f16(const Problem& p, const void* o, const void* dO, float* delta,
@@ -97,6 +102,7 @@ attn_status_t enqueue_bwd(const void* q, const void* k, const void* v, const voi
 
 // Tile constants of each kernel family, reported by attn_build_info().
 const char* fwd_bf16_tiles();
+const char* fwd64_tiles();
 const char* bwd_dkdv_tiles();
 const char* bwd_dq_tiles();
 const char* f32_tiles();

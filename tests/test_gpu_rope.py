@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_support import as_numpy, check_against, say, to_device
+from gpu_support import TOL, as_numpy, check_against, say, to_device
 from reproducible_causal_attention_amd import attn as A
 from reproducible_causal_attention_amd import workloads as W
 
@@ -82,22 +82,31 @@ def test_rope_edge_parity(case):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_identity_tables_give_the_plain_path(dtype):
-    """cos = 1, sin = 0 rotates nothing: the rotary entry points then return the
-    values of attn_fwd / attn_bwd exactly (a zero may change sign)."""
+    """cos = 1, sin = 0 rotates nothing.  The backward of the rotary path (its
+    preparation kernel and the shared dK/dV + dQ grid) then returns the values of
+    attn_bwd exactly when both are given the same forward outputs.  The forwards
+    are different kernels at head dim 64 (the plain one stages K/V by load-to-LDS
+    and has no register pass in which to rotate K, the rotary one rotates K in its
+    register-staged loads), each with its own fixed summation order, so they agree
+    to the rounding of the dtype rather than bitwise: o within the dtype's
+    tolerance relative to max |o|, lse within it in nats."""
     w = W.custom(2, 333, 12, 4, 64, dtype, seed=77)
     inp = W.generate(w)
     q, k, v, dO = to_device(inp)
     ones = torch.ones((w.T, 32), dtype=torch.float32, device=q.device)
     zeros = torch.zeros_like(ones)
+    tol = TOL[dtype]["o"]
     say("rope identity tables", w.label())
     for causal in (True, False):
         o, lse = A.fwd(q, k, v, w.scale, causal)
-        dq, dk, dv = A.bwd(q, k, v, o, lse, dO, w.scale, causal)
         o2, lse2 = A.fwd_rope(q, k, v, ones, zeros, w.scale, causal)
-        dq2, dk2, dv2 = A.bwd_rope(q, k, v, o2, lse2, dO, ones, zeros, w.scale, causal)
+        dq, dk, dv = A.bwd(q, k, v, o, lse, dO, w.scale, causal)
+        dq2, dk2, dv2 = A.bwd_rope(q, k, v, o, lse, dO, ones, zeros, w.scale, causal)
         torch.cuda.synchronize()
-        for n, a, b in (("o", o, o2), ("lse", lse, lse2), ("dq", dq, dq2), ("dk", dk, dk2),
-                        ("dv", dv, dv2)):
+        e_o = float((o.float() - o2.float()).abs().max() / o.float().abs().max())
+        e_l = float((lse - lse2).abs().max())
+        assert e_o <= tol and e_l <= tol, (causal, e_o, e_l)
+        for n, a, b in (("dq", dq, dq2), ("dk", dk, dk2), ("dv", dv, dv2)):
             assert torch.equal(a, b), (n, causal)
 
 
