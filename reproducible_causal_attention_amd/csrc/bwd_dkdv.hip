@@ -5,15 +5,15 @@
 namespace rca {
 namespace {
 
-template <class E, int kD>
+template <class E, int kD, bool kSolo>
 __global__ __launch_bounds__(dkdv::NTHREADS) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv,
     float scale, float scale_log2, int causal) {
   __shared__ __attribute__((aligned(16))) char smem[dkdv::Dims<kD>::SMEM_BYTES];
-  dkdv::unit_body<E, false, kD>(smem, blockIdx.x, q, k, v, dO, lse, delta, nullptr, nullptr, dk, dv, B,
-                            T, Hq, Hkv, scale, scale_log2, causal);
+  dkdv::run_unit<E, false, kD, kSolo>(smem, blockIdx.x, q, k, v, dO, lse, delta, nullptr, nullptr, dk, dv, B,
+                               T, Hq, Hkv, scale, scale_log2, causal);
 }
 
 }  // namespace
@@ -23,9 +23,10 @@ hipError_t launch_bwd_dkdv_e(const Problem& p, const void* q, const void* k, con
                                 const void* dO, const float* lse, const float* delta, void* dk,
                                 void* dv, hipStream_t s) {
   const int nkb = (p.T + 31) / 32;
-  const int npairs = (nkb + 1) / 2;
-  const dim3 grid((unsigned)(npairs * p.B * p.Hkv));
-  auto kernel = p.D == 128 ? attn_bwd_dkdv_kernel<E, 128> : attn_bwd_dkdv_kernel<E, 64>;
+  const dim3 grid((unsigned)(dkdv::units_per_group(p.Hq / p.Hkv, nkb, p.D) * p.B * p.Hkv));
+  auto kernel = p.D == 128 ? attn_bwd_dkdv_kernel<E, 128, false>
+                : dkdv::solo_units(p.Hq / p.Hkv, nkb, p.D) ? attn_bwd_dkdv_kernel<E, 64, true>
+                                                            : attn_bwd_dkdv_kernel<E, 64, false>;
   kernel<<<grid, dkdv::NTHREADS, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta,
@@ -47,7 +48,8 @@ hipError_t launch_bwd_dkdv_f16(const Problem& p, const void* q, const void* k, c
 }
 
 const char* bwd_dkdv_tiles() {
-  return "dkdv_bf16{key_block=32,waves=8,pairs=(j,n-1-j),query_step=32,mfma=32x32x16,lds_dma_x2,D=64|128(x1)}";
+  return "dkdv_bf16{key_block=32,waves=8,pairs=(j,n-1-j),query_step=32,mfma=32x32x16,lds_dma_x2,D=64|128(x1),"
+         "per-wave pairs when G*(nkb+1)<=48 (D=64)}";
 }
 
 }  // namespace rca

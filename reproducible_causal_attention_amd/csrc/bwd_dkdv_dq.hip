@@ -32,7 +32,7 @@ constexpr int smem_bytes() {
 // workgroups the two kinds land on different workgroups).  Every unit is taken
 // exactly once, and each computes exactly what it computes in its own kernel,
 // so the results do not depend on P.
-template <class E, bool kRope, int kD>
+template <class E, bool kRope, int kD, bool kSolo>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -50,8 +50,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_dq_kernel(
     __syncthreads();  // the next unit reuses the LDS
   }
   for (int u = x + 8 * (Q - 1 - l); u < n_kv; u += 8 * Q) {
-    dkdv::unit_body<E, kRope, kD>(smem, u, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T, Hq,
-                                  Hkv, scale, scale_log2, causal);
+    dkdv::run_unit<E, kRope, kD, kSolo>(smem, u, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T, Hq,
+                                 Hkv, scale, scale_log2, causal);
     __syncthreads();
   }
 }
@@ -65,7 +65,7 @@ hipError_t launch_bwd_dkdv_dq_e(const Problem& p, const void* q, const void* k, 
                                 hipStream_t s) {
   const int n_dq = ((p.T + dqb::BM - 1) / dqb::BM) * p.B * p.Hq;
   const int nkb = (p.T + 31) / 32;
-  const int n_kv = (nkb + 1) / 2 * p.B * p.Hkv;
+  const int n_kv = dkdv::units_per_group(p.Hq / p.Hkv, nkb, p.D) * p.B * p.Hkv;
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -74,7 +74,9 @@ hipError_t launch_bwd_dkdv_dq_e(const Problem& p, const void* q, const void* k, 
   // per unit with a margin of two per XCD when the units are fewer.
   const int units = n_dq + n_kv + 16;
   const int P = ((n_cu < units ? n_cu : units) + 7) / 8 * 8;
-  auto kernel = p.D == 128 ? attn_bwd_dkdv_dq_kernel<E, kRope, 128> : attn_bwd_dkdv_dq_kernel<E, kRope, 64>;
+  auto kernel = p.D == 128 ? attn_bwd_dkdv_dq_kernel<E, kRope, 128, false>
+                : dkdv::solo_units(p.Hq / p.Hkv, nkb, p.D) ? attn_bwd_dkdv_dq_kernel<E, kRope, 64, true>
+                                                            : attn_bwd_dkdv_dq_kernel<E, kRope, 64, false>;
   kernel<<<dim3((unsigned)P), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta, rcos, rsin,

@@ -407,5 +407,243 @@ __device__ __forceinline__ void unit_body(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Per-wave units (64-wide heads).  When a pair of key blocks has few steps --
+// G * (nkb + 1) <= kSoloMaxSteps, e.g. multi-head attention at T = 1024 has 33 --
+// splitting them over eight waves leaves each wave a handful of steps behind
+// the unit's shared prologue (K/V staging, a barrier) and epilogue (partials
+// parked in LDS, a barrier, a sum over the waves).  Then each wave owns a pair
+// (j, n-1-j) of key blocks outright: it loads a block's K and V operands
+// straight into registers, runs all of the block's steps (query heads of the
+// group, then query blocks, in order) with its own double-buffered row copies,
+// and writes dK (scaled) and dV from its accumulators, one block after the
+// other.  No barrier, no cross-wave sum.  Workgroup unit u of a (batch, KV head)
+// group takes pairs 8u + w (w = wave); the choice depends only on G and T, so
+// batch and group slicing keep their bits.
+constexpr int kSoloMaxSteps = 48;
+__host__ __device__ constexpr bool solo_units(int G, int nkb, int D) {
+  return D == 64 && G * (nkb + 1) <= kSoloMaxSteps;
+}
+// Workgroup units of dK/dV work: pairs of key blocks (split design) or groups of
+// eight pairs (per-wave design), per (batch, KV head).
+__host__ __device__ constexpr int units_per_group(int G, int nkb, int D) {
+  return solo_units(G, nkb, D) ? ((nkb + 1) / 2 + NWAVES - 1) / NWAVES : (nkb + 1) / 2;
+}
+
+template <class E, bool kRope>
+__device__ __forceinline__ void solo_body(
+    char* __restrict__ smem, int unit, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
+    int causal) {
+  constexpr int kD = 64;
+  using Dm = Dims<kD>;
+  constexpr int NQ = Dm::NQ, ND = Dm::ND, ROWS_BYTES = Dm::ROWS_BYTES;
+  constexpr int BUF_BYTES = Dm::BUF_BYTES, WAVE_BYTES = Dm::WAVE_BYTES;
+  constexpr uint32_t kHalf = kD / 2;  // rotary pairs per row
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int nkb = (T + 31) / 32;
+  const int npairs = (nkb + 1) / 2;
+  const int G = Hq / Hkv;
+  int bg, r;
+  decode_unit(unit, B * Hkv, bg, r);  // r: workgroup unit within the group
+  const int pair = NWAVES * r + wave;
+  if (pair >= npairs) return;  // a group's last workgroup unit may hold fewer pairs
+  const int b = bg / Hkv;
+  const int kvh = bg - b * Hkv;
+
+  const uint32_t q_row = (uint32_t)Hq * kD * 2;
+  const uint32_t kv_row = (uint32_t)Hkv * kD * 2;
+  const size_t qe = (size_t)T * Hq * kD, ke = (size_t)T * Hkv * kD;
+  const rsrc_t rk = make_rsrc(k + b * ke, (uint32_t)T * kv_row);
+  const rsrc_t rv = make_rsrc(v + b * ke, (uint32_t)T * kv_row);
+  const rsrc_t rdk = make_rsrc(dk + b * ke, (uint32_t)T * kv_row);
+  const rsrc_t rdv = make_rsrc(dv + b * ke, (uint32_t)T * kv_row);
+  const u32x4_t q_src = raw_rsrc(q + b * qe, (uint32_t)T * q_row);
+  const u32x4_t do_src = raw_rsrc(dO + b * qe, (uint32_t)T * q_row);
+  const rsrc_t rl = make_rsrc(lse + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
+  const rsrc_t rd = make_rsrc(delta + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
+
+  char* const my_region = smem + wave * WAVE_BYTES;
+  const int dma_row = lane >> 3;
+  uint32_t row_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    row_off[i] = (uint32_t)(8 * i + dma_row) * q_row + 16u * (uint32_t)swz_slot(8 * i + dma_row, lane & 7);
+
+  const int jA = pair, jB = nkb - 1 - pair;
+  for (int pass = 0; pass < (jA == jB ? 1 : 2); ++pass) {
+    const int j = pass == 0 ? jA : jB;
+    const int k0 = 32 * j;
+    const int my_key = k0 + l32;
+    const int qb0 = causal ? j : 0;
+    const int per_head = nkb - qb0;
+    const int nsteps = G * per_head;
+
+    // Step s: rows 32*qb .. +31 of query head h of the group into buffer buf.
+    auto issue_step = [&](int s, int buf, float& l_raw, float& d_raw) {
+      const int hh = s / per_head;
+      const int qb = qb0 + (s - hh * per_head);
+      const int h = kvh * G + hh;
+      char* dst = my_region + buf * BUF_BYTES;
+      const uint32_t step_off = (uint32_t)(32 * qb) * q_row + (uint32_t)h * kD * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dma16s(q_src, dst + 1024 * i, row_off[i], step_off);
+        dma16s(do_src, dst + ROWS_BYTES + 1024 * i, row_off[i], step_off);
+      }
+      const uint32_t soff = ((uint32_t)h * T + 32 * qb + l32) * 4;
+      l_raw = bload_f32(rl, soff);
+      d_raw = bload_f32(rd, soff);
+    };
+
+    // K and V of the block as B operands (keys on the lanes, d = 16c + 8g + [0, 8)),
+    // straight from memory; rows past T read as zero.
+    u32x4_t kf[NQ], vf[NQ];
+    const uint32_t kv_off = (uint32_t)my_key * kv_row + (uint32_t)kvh * kD * 2 + 16u * (uint32_t)g;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      kf[c] = bload16(rk, kv_off + 32 * c);
+      vf[c] = bload16(rv, kv_off + 32 * c);
+    }
+    float l_raw = 0.f, d_raw = 0.f;
+    issue_step(0, 0, l_raw, d_raw);  // every block has at least one step
+    f32x16_t dk_acc[ND], dv_acc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) dk_acc[db] = dv_acc[db] = zero16();
+
+    int buf = 0;
+    for (int s = 0; s < nsteps; ++s, buf ^= 1) {
+      const int hh = s / per_head;
+      const int q0 = 32 * (qb0 + (s - hh * per_head));
+      char* cur = my_region + buf * BUF_BYTES;
+      const uint16_t* sQ = reinterpret_cast<const uint16_t*>(cur);
+      const uint16_t* sdO = reinterpret_cast<const uint16_t*>(cur + ROWS_BYTES);
+      float* stat = reinterpret_cast<float*>(cur + 2 * ROWS_BYTES);  // [0,32): lse*log2e, [32,64): -delta
+
+      wait_vmem();  // this step's rows and statistics (issued one step ago), and K/V
+      stat[lane] = g == 0 ? l_raw * kLog2e : -d_raw;
+      if (s + 1 < nsteps) issue_step(s + 1, buf ^ 1, l_raw, d_raw);
+      wave_lds_fence();
+
+      f32x16_t pacc, Lr;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float4 d4 = *reinterpret_cast<const float4*>(stat + 32 + 8 * jj + 4 * g);
+        const float4 l4 = *reinterpret_cast<const float4*>(stat + 8 * jj + 4 * g);
+        pacc[4 * jj + 0] = d4.x; pacc[4 * jj + 1] = d4.y; pacc[4 * jj + 2] = d4.z; pacc[4 * jj + 3] = d4.w;
+        Lr[4 * jj + 0] = l4.x; Lr[4 * jj + 1] = l4.y; Lr[4 * jj + 2] = l4.z; Lr[4 * jj + 3] = l4.w;
+      }
+      f32x16_t sacc = zero16();
+      u32x4_t da[NQ], ta[ND][4];
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) da[c] = lds_load16_swz(sdO, l32, 16 * c + 8 * g);
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) sacc = E::mfma(lds_load16_swz(sQ, l32, 16 * c + 8 * g), kf[c], sacc);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        ta[db][0] = lds_operand_T_swz(sdO, 0, 32 * db, lane);
+        ta[db][1] = lds_operand_T_swz(sdO, 16, 32 * db, lane);
+        ta[db][2] = lds_operand_T_swz(sQ, 0, 32 * db, lane);
+        ta[db][3] = lds_operand_T_swz(sQ, 16, 32 * db, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) pacc = E::mfma(da[c], vf[c], pacc);  // dP - delta
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sacc[rr] = fast_exp2(fmaf(sacc[rr], scale_log2, -Lr[rr]));
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Register rr is query q0 + 8*(rr/4) + 4g + rr%4 against key my_key: P = 0 where
+      // the key is after the query (diagonal block) or the query row does not exist.
+      if ((causal && q0 == k0) || q0 + 31 >= T) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int qi = q0 + 8 * (rr >> 2) + 4 * g + (rr & 3);
+          if ((causal && my_key > qi) || qi >= T) sacc[rr] = 0.f;
+        }
+      }
+      const u32x4_t pb0 = pack_operand_e<E>(sacc, 0), pb1 = pack_operand_e<E>(sacc, 8);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        dv_acc[db] = E::mfma(ta[db][0], pb0, dv_acc[db]);
+        dv_acc[db] = E::mfma(ta[db][1], pb1, dv_acc[db]);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) pacc[rr] *= sacc[rr];
+      const u32x4_t sb0 = pack_operand_e<E>(pacc, 0), sb1 = pack_operand_e<E>(pacc, 8);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        dk_acc[db] = E::mfma(ta[db][2], sb0, dk_acc[db]);
+        dk_acc[db] = E::mfma(ta[db][3], sb1, dk_acc[db]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
+#pragma unroll
+      for (int i = 0; i < 2 * ND; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * ND, 1);
+      wave_lds_fence();  // this buffer's reads complete before it is refilled
+    }
+
+    // dK^T, dV^T: lane holds key my_key, d = 32db + 8jj + 4g + 0..3 in registers 4jj..4jj+3.
+    // Rows past the sequence end are dropped by the buffer range check.
+    const uint32_t out_row = (uint32_t)my_key * kv_row + (uint32_t)kvh * kD * 2;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * db + 8 * jj + 4 * g;
+        float g0 = dk_acc[db][4 * jj] * scale, g1 = dk_acc[db][4 * jj + 1] * scale;
+        float g2 = dk_acc[db][4 * jj + 2] * scale, g3 = dk_acc[db][4 * jj + 3] * scale;
+        if (kRope) {  // pairs d0/2 and d0/2 + 1 of key my_key
+          const rsrc_t rtc = make_rsrc(rcos, (uint32_t)T * kHalf * 4u);
+          const rsrc_t rts = make_rsrc(rsin, (uint32_t)T * kHalf * 4u);
+          const uint32_t toff = ((uint32_t)my_key * kHalf + d0 / 2) * 4;
+          rope_rotate_back(g0, g1, bload_f32(rtc, toff), bload_f32(rts, toff));
+          rope_rotate_back(g2, g3, bload_f32(rtc, toff + 4), bload_f32(rts, toff + 4));
+        }
+        u32x2_t wk, wv;
+        wk[0] = E::pack2(g0, g1);
+        wk[1] = E::pack2(g2, g3);
+        wv[0] = E::pack2(dv_acc[db][4 * jj], dv_acc[db][4 * jj + 1]);
+        wv[1] = E::pack2(dv_acc[db][4 * jj + 2], dv_acc[db][4 * jj + 3]);
+        bstore8(rdk, out_row + 2 * d0, wk);
+        bstore8(rdv, out_row + 2 * d0, wv);
+      }
+    }
+  }
+}
+
+// Workgroup unit u of the dK/dV work in the design the launcher chose
+// (kSolo == solo_units(G, nkb, kD), decided on the host).
+template <class E, bool kRope, int kD, bool kSolo>
+__device__ __forceinline__ void run_unit(
+    char* __restrict__ smem, int unit, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
+    int causal) {
+  if constexpr (kSolo && kD == 64)
+    solo_body<E, kRope>(smem, unit, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T, Hq, Hkv,
+                        scale, scale_log2, causal);
+  else
+    unit_body<E, kRope, kD>(smem, unit, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T, Hq, Hkv,
+                            scale, scale_log2, causal);
+}
+
 }  // namespace dkdv
 }  // namespace rca
