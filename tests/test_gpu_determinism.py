@@ -94,9 +94,14 @@ def test_same_bits_under_cu_masks(mask_kind):
     assert got == want
 
 
-def test_batch_invariance():
-    """Element b computed alone equals slice b of the batched call, bitwise."""
-    w = W.custom(4, 700, 6, 2, 64, "bf16", seed=21)
+@pytest.mark.parametrize("shape", [(4, 700, 6, 2), (4, 700, 4, 4)],
+                         ids=["gqa-split-dkdv-units", "mha-per-wave-dkdv-units"])
+def test_batch_invariance(shape):
+    """Element b computed alone equals slice b of the batched call, bitwise (with
+    three query heads per KV head the dK/dV work is split over the eight waves of a
+    unit; with one, each wave owns a pair of key blocks)."""
+    B, T, Hq, Hkv = shape
+    w = W.custom(B, T, Hq, Hkv, 64, "bf16", seed=21)
     inp = W.generate(w)
     q, k, v, dO = to_device(inp)
     say("batch invariance", w.label())
@@ -126,16 +131,19 @@ def test_forward_tile_size_does_not_change_bits(D):
         assert torch.equal(lse_one[0], lse_full[b]), b
 
 
-def test_kv_group_invariance():
-    """One KV-head group computed alone equals its slice of the GQA call, bitwise
+@pytest.mark.parametrize("shape", [(2, 513, 12, 4), (2, 513, 8, 8)],
+                         ids=["gqa-split-dkdv-units", "mha-per-wave-dkdv-units"])
+def test_kv_group_invariance(shape):
+    """One KV-head group computed alone equals its slice of the call, bitwise
     (the head-parallel split of a sharded run)."""
-    w = W.custom(2, 513, 12, 4, 64, "bf16", seed=22)
+    B, T, Hq, Hkv = shape
+    w = W.custom(B, T, Hq, Hkv, 64, "bf16", seed=22)
     inp = W.generate(w)
     q, k, v, dO = to_device(inp)
     say("group invariance", w.label())
     full = run_gpu(inp, (q, k, v, dO))
-    G = 3
-    for g in (0, 2):
+    G = Hq // Hkv
+    for g in (0, Hkv - 1):
         hs = slice(g * G, (g + 1) * G)
         part = run_gpu(inp, (q[:, :, hs].contiguous(), k[:, :, g:g + 1].contiguous(),
                              v[:, :, g:g + 1].contiguous(), dO[:, :, hs].contiguous()))
