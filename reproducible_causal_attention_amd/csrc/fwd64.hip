@@ -13,10 +13,15 @@
 // softmax: one exponential per score) as matrix work, and a wave that owns only 32
 // queries re-reads every K/V row from LDS for each 32 queries, so the forward was
 // bound by LDS reads and by matrix and vector work that did not overlap.  Here:
-//   * a workgroup of 4 waves owns 128 query rows of one (batch, query head): two
-//     64-row query groups times two key halves, and two workgroups share a CU;
-//   * each wave keeps 64 queries (two 32-row blocks) against the same K/V rows, so
-//     every K/V operand read from LDS feeds two products;
+//   * a workgroup owns 128 query rows of one (batch, query head), split between
+//     two key halves and, within each, between query groups: on grids that fit
+//     the GPU in one round (at most twice the CU count) 8 waves of 32 rows each,
+//     one workgroup per CU, or two when the grid exceeds the CU count (the kernel
+//     then held to 128 registers), so a heavy query tile's softmax (vector work a
+//     single wave issues slowly) is spread over eight waves; on larger grids 4
+//     waves of 64 rows each, two workgroups per CU, so every K/V operand read
+//     from LDS feeds two products.  A row's arithmetic is the same in every form,
+//     so all forms give the same bits;
 //   * K/V tiles of 128 keys go straight from HBM into double-buffered LDS
 //     (buffer_load ... lds, no staging registers; 16-byte chunks XOR-swizzled so
 //     row reads and transposed reads are free of bank conflicts), and the per-lane
@@ -28,10 +33,10 @@
 //   * a block's probabilities are computed against the running max without
 //     first taking the block's own maximum (one fma, one exponential, half a pack
 //     and half a pair-sum per score); a block where some lane's share of a row
-//     sum exceeds 2^8 (its max grew, or the row had none yet) is redone with its
-//     max taken, the running max moved up to an integer and O and the row sum
-//     multiplied by the exact power of two; its P V products are issued only
-//     after that check;
+//     sum exceeds 2^8 (its max grew, or the row had none yet) is redone, per
+//     32-row query block, with its max taken, the running max moved up to an
+//     integer and O and the row sum multiplied by the exact power of two; its
+//     P V products are issued only after that check;
 //   * within a tile the products of one block are interleaved with the
 //     exponentials of the other (block B's score products with block A's softmax,
 //     block A's P V products with block B's softmax), so the matrix and vector
@@ -49,8 +54,6 @@ namespace rca {
 namespace {
 
 constexpr int BM = 128;                 // query rows per workgroup
-constexpr int NW = 4;                   // waves per workgroup
-constexpr int NT = NW * 64;
 constexpr int BN = 128;                 // keys per K/V tile
 constexpr int TBYTES = BN * 128;        // one tile of one tensor: 128 rows of 128 bytes
 constexpr int BUF_BYTES = 2 * TBYTES;   // K then V
@@ -101,8 +104,14 @@ __device__ __forceinline__ int opaque(int x) {
 }
 constexpr int key_off(int r) { return 8 * (r >> 2) + (r & 3); }
 
-template <bool kPosScale, class E>
-__global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
+// kQB: 32-row query blocks per wave (1: 8 waves per workgroup, 2: 4 waves); kWaves:
+// waves per SIMD the kernel's registers must allow.  Each row is computed the same
+// way in every instantiation (same products, same order, its own slow path), so
+// all of them give the same bits.
+template <int kQB>
+constexpr int threads_of() { return 64 * 8 / kQB; }
+template <bool kPosScale, class E, int kQB, int kWaves>
+__global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv,
     float scale_log2, int causal) {
@@ -112,8 +121,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
   const int wave = wave_id();
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int qg = wave & 1;   // query group: rows 64qg .. +63 of the tile
-  const int kh = wave >> 1;  // key half: blocks 32kh and 64 + 32kh of every tile
+  constexpr int QB = kQB;
+  constexpr int NW = 8 / QB;       // waves per workgroup
+  constexpr int NQG = NW / 2;      // query groups (32*QB rows each) per workgroup
+  const int qg = wave % NQG;       // query group: rows 32*QB*qg .. of the tile
+  const int kh = wave / NQG;       // key half: blocks 32kh and 64 + 32kh of every tile
 
   const int G = Hq / Hkv;
   const int n_qt = (T + BM - 1) / BM;
@@ -134,18 +146,18 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
   const u32x4_t k_src = raw_rsrc(k + b * ke, (uint32_t)T * kv_row);
   const u32x4_t v_src = raw_rsrc(v + b * ke, (uint32_t)T * kv_row);
 
-  const int qw0 = qt * BM + 64 * qg;  // first query row of this wave
+  const int qw0 = qt * BM + 32 * QB * qg;  // first query row of this wave
   // Q^T as B operands: lane holds query qw0 + 32qb + l32, d = 16s + 8g + [0, 8).
-  u32x4_t qf[2][4];
-  uint32_t qoff[2];
+  u32x4_t qf[QB][4];
+  uint32_t qoff[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     qoff[qb] = (uint32_t)(qw0 + 32 * qb + l32) * q_row + (uint32_t)h * 128;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[qb][s] = bload16(rq, qoff[qb] + 32 * s + 16 * g);
   }
 
-  // Tile copy: instruction (tensor, group of 8 rows) with group = wave + 4m, so a
+  // Tile copy: instruction (tensor, group of 8 rows) with group = wave + NW*m, so a
   // wave's groups all have the parity of `wave` and one per-lane offset serves
   // them: lane fills slot lane%8 of row 8*group + lane/8, i.e. fetches chunk
   // (lane%8) ^ swz(row).
@@ -160,8 +172,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
   auto copy_tile = [&](int t, int buf) {
     const bool present = t < n_kv;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int grp = wave + 4 * m;
+    for (int m = 0; m < 16 / NW; ++m) {
+      const int grp = wave + NW * m;
       // out of range (zeros, no traffic) after the last tile
       const uint32_t soff = present ? (uint32_t)(t * BN + 8 * grp) * kv_row : 0x80000000u;
       const uint32_t dst = lds0 + (uint32_t)(buf * BUF_BYTES + grp * 1024);
@@ -198,11 +210,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
   copy_tile(0, 0);  // in flight together with the Q rows
   wait_vmem();
 
-  f32x16_t oacc[2][2];  // O^T [db][qb]: rows d = 32db + 8*(r/4) + 4g + r%4, column = query
+  f32x16_t oacc[2][QB];  // O^T [db][qb]: rows d = 32db + 8*(r/4) + 4g + r%4, column = query
 #pragma unroll
-  for (int db = 0; db < 2; ++db) oacc[db][0] = oacc[db][1] = zero16();
-  float m_run[2] = {-1e30f, -1e30f};  // running max per query (base-2 units; an integer once set)
-  float l_run[2] = {0.f, 0.f};        // this lane's share of the running sum
+  for (int db = 0; db < 2; ++db)
+    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = zero16();
+  float m_run[QB];  // running max per query (base-2 units; an integer once set)
+  float l_run[QB];        // this lane's share of the running sum
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -1e30f; l_run[qb] = 0.f; }
 
   __syncthreads();
 
@@ -212,20 +226,25 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
     const int last = causal ? min(qw0 + 32 * qb + l32, T - 1) : T - 1;
     return last - kb0 - 4 * g;
   };
-  // Score products of one 32-key block (tile rows krow .. +31) for both query blocks.
-  auto s_block = [&](const char* sK, int krow, f32x16_t (&sacc)[2]) {
-    u32x4_t kop[4];
+  // Score products of one 32-key block (tile rows krow .. +31): for every query
+  // block, or (s_one) for query block qb alone.
+  auto k_operands = [&](const char* sK, int krow, u32x4_t (&kop)[4]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) kop[s] = *reinterpret_cast<const u32x4_t*>(sK + krow * 128 + ka[s]);
+  };
+  auto s_one = [&](const u32x4_t (&kop)[4], int qb, f32x16_t& acc) {
+    acc = zero16();
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sacc[qb] = zero16();
+    for (int s = 0; s < 4; ++s) acc = E::mfma(kop[s], qf[qb][s], acc);
+  };
+  auto s_block = [&](const char* sK, int krow, f32x16_t (&sacc)[QB]) {
+    u32x4_t kop[4];
+    k_operands(sK, krow, kop);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sacc[qb] = E::mfma(kop[s], qf[qb][s], sacc[qb]);
-    }
+    for (int qb = 0; qb < QB; ++qb) s_one(kop, qb, sacc[qb]);
   };
   // P V products of one block: O^T[db][qb] += V^T(keys krow..) P^T.
-  auto pv_block = [&](const char* sV, int krow, const u32x4_t (&p)[2][2]) {
+  auto pv_block = [&](const char* sV, int krow, const u32x4_t (&p)[QB][2]) {
     u32x4_t vop[2][2];
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
@@ -236,7 +255,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         oacc[db][qb] = E::mfma(vop[db][0], p[qb][0], oacc[db][qb]);
         oacc[db][qb] = E::mfma(vop[db][1], p[qb][1], oacc[db][qb]);
       }
@@ -247,80 +266,83 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
   // kb0 + 8*(r/4) + 4g + r%4 against query qw0 + 32qb + l32; kEdge: the block
   // crosses the diagonal or the sequence end, so keys after the query or past T
   // get probability 0.
-  auto exp_block = [&](f32x16_t (&sacc)[2], int kb0, auto edge_c, u32x4_t (&p)[2][2]) {
+  auto exp_one = [&](f32x16_t& acc, int kb0, auto edge_c, int qb, u32x4_t (&p)[2]) {
     constexpr bool kEdge = decltype(edge_c)::value;
+    const int lim = kEdge ? opaque(edge_limit(kb0, qb)) : 0;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int lim = kEdge ? opaque(edge_limit(kb0, qb)) : 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(fmaf(sacc[qb][r], scale_log2, -m_run[qb]));
-        sacc[qb][r] = (kEdge && key_off(r) > lim) ? 0.f : pr;
-      }
-      p[qb][0] = pack_operand_e<E>(sacc[qb], 0);
-      p[qb][1] = pack_operand_e<E>(sacc[qb], 8);
+    for (int r = 0; r < 16; ++r) {
+      const float pr = fast_exp2(fmaf(acc[r], scale_log2, -m_run[qb]));
+      acc[r] = (kEdge && key_off(r) > lim) ? 0.f : pr;
     }
+    p[0] = pack_operand_e<E>(acc, 0);
+    p[1] = pack_operand_e<E>(acc, 8);
+  };
+  auto exp_block = [&](f32x16_t (&sacc)[QB], int kb0, auto edge_c, u32x4_t (&p)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) exp_one(sacc[qb], kb0, edge_c, qb, p[qb]);
   };
   // This lane's share (its 16 of the block's 32 keys) of each query's sum of the
   // packed probabilities of a block (the values that enter O), two per
   // v_dot2c_f32 against ones.
-  auto sum_block = [&](const u32x4_t (&p)[2][2], float (&bs)[2]) {
+  auto sum_one = [&](const u32x4_t (&p)[2]) {
+    float acc = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float acc = 0.f;
+    for (int i = 0; i < 4; ++i) acc = E::add_pair(p[1][i], E::add_pair(p[0][i], acc));
+    return acc;
+  };
+  auto sum_block = [&](const u32x4_t (&p)[QB][2], float (&bs)[QB]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = E::add_pair(p[qb][1][i], E::add_pair(p[qb][0][i], acc));
-      bs[qb] = acc;
-    }
+    for (int qb = 0; qb < QB; ++qb) bs[qb] = sum_one(p[qb]);
   };
   // Row maxima of a block's scores (masked as in exp_block) and the move of the
   // running max: a row whose maximum exceeds it moves it up to the next integer at
   // or above that maximum, and its O and running sum are multiplied by the exact
   // power of two 2^(m_old - m_new) (0 at the first visible block).
-  auto max_and_rescale = [&](const f32x16_t (&sacc)[2], int kb0, auto edge_c) {
+  auto max_rescale_one = [&](const f32x16_t& acc, int kb0, auto edge_c, int qb) {
     constexpr bool kEdge = decltype(edge_c)::value;
+    float mraw = kPosScale ? -__builtin_inff() : __builtin_inff();
+    const int lim = kEdge ? opaque(edge_limit(kb0, qb)) : 0;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mraw = kPosScale ? -__builtin_inff() : __builtin_inff();
-      const int lim = kEdge ? opaque(edge_limit(kb0, qb)) : 0;
+    for (int r = 0; r < 16; ++r) {
+      float x = acc[r];
+      if (kEdge && key_off(r) > lim) x = kPosScale ? -__builtin_inff() : __builtin_inff();
+      mraw = kPosScale ? fmaxf(mraw, x) : fminf(mraw, x);
+    }
+    const float mx = halves_max(mraw * scale_log2);
+    const float m_new = mx > m_run[qb] ? ceilf(mx) : m_run[qb];
+    const float d = m_run[qb] - m_new;  // 0, a negative integer, or about -1e30 at the start
+    const float alpha = d < -126.f ? 0.f : __builtin_ldexpf(1.0f, (int)d);
+    m_run[qb] = m_new;
+    l_run[qb] *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[qb][r];
-        if (kEdge && key_off(r) > lim) x = kPosScale ? -__builtin_inff() : __builtin_inff();
-        mraw = kPosScale ? fmaxf(mraw, x) : fminf(mraw, x);
-      }
-      const float mx = halves_max(mraw * scale_log2);
-      const float m_new = mx > m_run[qb] ? ceilf(mx) : m_run[qb];
-      const float d = m_run[qb] - m_new;  // 0, a negative integer, or about -1e30 at the start
-      const float alpha = d < -126.f ? 0.f : __builtin_ldexpf(1.0f, (int)d);
-      m_run[qb] = m_new;
-      l_run[qb] *= alpha;
+    for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
-      }
+      for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
     }
   };
   // A block's probabilities were computed against the running max without looking
   // at the block's own maximum.  If some lane's share of a row's block sum exceeds
   // 2^8 (so some probability may exceed 2^8, or overflowed, or the row had no
-  // running max yet) the block is redone: its scores recomputed, the running max
+  // running max yet) the block is redone for that 32-row query block (whichever
+  // wave holds it): its scores recomputed, the running max
   // moved and O rescaled, its probabilities and sums recomputed.  Then the sums
   // are added.
   // Its P V products are issued only after this, so O stays consistent.
-  auto settle_block = [&](const char* sK, int krow, int kb0, auto edge_c, u32x4_t (&p)[2][2],
-                          float (&bs)[2]) {
-    const bool big = !(bs[0] <= kSumLimit) || !(bs[1] <= kSumLimit);
-    if (__any(big)) {
-      f32x16_t sacc[2];
-      s_block(sK, krow, sacc);
-      max_and_rescale(sacc, kb0, edge_c);
-      exp_block(sacc, kb0, edge_c, p);
-      sum_block(p, bs);
+  auto settle_block = [&](const char* sK, int krow, int kb0, auto edge_c, u32x4_t (&p)[QB][2],
+                          float (&bs)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {  // each 32-row query block on its own
+      if (__any(!(bs[qb] <= kSumLimit))) {
+        u32x4_t kop[4];
+        f32x16_t acc;
+        k_operands(sK, krow, kop);
+        s_one(kop, qb, acc);
+        max_rescale_one(acc, kb0, edge_c, qb);
+        exp_one(acc, kb0, edge_c, qb, p[qb]);
+        bs[qb] = sum_one(p[qb]);
+      }
+      l_run[qb] += bs[qb];
     }
-    l_run[0] += bs[0];
-    l_run[1] += bs[1];
   };
 
   // One tile: blocks A (keys 32kh) and B (keys 64 + 32kh) of the tile in buffer BUF.
@@ -331,9 +353,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
     const char* sV = sK + TBYTES;
     const int krA = 32 * kh, krB = 64 + 32 * kh;
     const int kbA = t * BN + krA, kbB = t * BN + krB;
-    f32x16_t sA[2], sB[2];
-    u32x4_t pA[2][2], pB[2][2];
-    float bsA[2], bsB[2];
+    f32x16_t sA[QB], sB[QB];
+    u32x4_t pA[QB][2], pB[QB][2];
+    float bsA[QB], bsB[QB];
     s_block(sK, krA, sA);
     __builtin_amdgcn_sched_barrier(0);
     // block B's score products with block A's exponentials
@@ -390,33 +412,35 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
   }
 
   // Merge the key halves: (m, l, O) of half 1 into half 0, in that order.  Half 1
-  // parks its state as [query group][float4 index f][lane] (f < 16: O^T registers
-  // 4f .. 4f+3 of oacc[f/8][(f/4)%2]; f = 16: m0, m1, l0, l1).
-  float4* part = reinterpret_cast<float4*>(smem) + qg * 17 * 64 + lane;
+  // parks its state as [query block][float4 index f][lane] (f < NF: O^T registers
+  // 4(f%4) .. +3 of oacc[f/(4QB)][(f/4)%QB]; f = NF: the first and last query
+  // block's m, then their l).
+  constexpr int NF = 2 * QB * 4;  // float4 per lane of O^T
+  float4* part = reinterpret_cast<float4*>(smem) + qg * (NF + 1) * 64 + lane;
   if (kh == 1) {
 #pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      const f32x16_t& a = oacc[f >> 3][(f >> 2) & 1];
+    for (int f = 0; f < NF; ++f) {
+      const f32x16_t& a = oacc[f / (4 * QB)][(f / 4) % QB];
       const int r = 4 * (f & 3);
       part[f * 64] = make_float4(a[r], a[r + 1], a[r + 2], a[r + 3]);
     }
-    part[16 * 64] = make_float4(m_run[0], m_run[1], l_run[0], l_run[1]);
+    part[NF * 64] = make_float4(m_run[0], m_run[QB - 1], l_run[0], l_run[QB - 1]);
   }
   __syncthreads();
   if (kh == 0) {
-    const float4 st = part[16 * 64];
-    const float m1[2] = {st.x, st.y}, l1[2] = {st.z, st.w};
+    const float4 st = part[NF * 64];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m = fmaxf(m_run[qb], m1[qb]);
-      const float a0 = fast_exp2(m_run[qb] - m), a1 = fast_exp2(m1[qb] - m);
-      const float l_tot = halves_sum(l_run[qb] * a0 + l1[qb] * a1);
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m1 = qb == 0 ? st.x : st.y, l1 = qb == 0 ? st.z : st.w;
+      const float m = fmaxf(m_run[qb], m1);
+      const float a0 = fast_exp2(m_run[qb] - m), a1 = fast_exp2(m1 - m);
+      const float l_tot = halves_sum(l_run[qb] * a0 + l1 * a1);
       const float inv = 1.0f / l_tot;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float4 x = part[(8 * db + 4 * qb + j) * 64];
+          const float4 x = part[(4 * QB * db + 4 * qb + j) * 64];
           u32x2_t w;
           w[0] = E::pack2((oacc[db][qb][4 * j + 0] * a0 + x.x * a1) * inv,
                           (oacc[db][qb][4 * j + 1] * a0 + x.y * a1) * inv);
@@ -434,19 +458,44 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd64_kernel(
 }  // namespace
 
 const char* fwd64_tiles() {
-  return "fwd64{BM=128,BN=128,waves=4(2 query groups of 64 x 2 key halves),2 workgroups/CU,"
-         "lds_dma_x2,mfma=32x32x16}";
+  return "fwd64{BM=128,BN=128,grids<=2*CUs: waves=8(4 query blocks of 32 x 2 key halves),"
+         "1 workgroup/CU (grid<=CUs) else 2 (128 VGPRs); larger grids: waves=4(2 query "
+         "groups of 64 x 2 key halves),2 workgroups/CU;lds_dma_x2,mfma=32x32x16}";
 }
 
 template <class E>
 hipError_t launch_fwd64_e(const Problem& p, const void* q, const void* k, const void* v, void* o,
                           float* lse, hipStream_t s) {
   const int n_qt = (p.T + BM - 1) / BM;
-  const dim3 grid((unsigned)(n_qt * p.B * p.Hq));
-  auto kernel = p.scale_log2 >= 0.f ? attn_fwd64_kernel<true, E> : attn_fwd64_kernel<false, E>;
-  kernel<<<grid, NT, 0, s>>>(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                             static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, p.B,
-                             p.T, p.Hq, p.Hkv, p.scale_log2, p.causal);
+  const long long n_wg = (long long)n_qt * p.B * p.Hq;
+  const dim3 grid((unsigned)n_wg);
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipGetLastError();
+  // Every instantiation gives the same bits; the choice is speed only.  Grids that
+  // fit the GPU in one round take 8-wave workgroups of 32-row waves (one per CU with
+  // the full register file, or two per CU at 128 registers): the heavy query tiles'
+  // softmax is spread over more waves.  Larger grids take 4-wave workgroups of
+  // 64-row waves, whose K/V operands each feed two products.
+  using K = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, int,
+                     int, int, int, float, int);
+  const bool pos = p.scale_log2 >= 0.f;
+  K kernel;
+  int threads;
+  if (n_wg <= n_cu) {
+    kernel = pos ? attn_fwd64_kernel<true, E, 1, 2> : attn_fwd64_kernel<false, E, 1, 2>;
+    threads = threads_of<1>();
+  } else if (n_wg <= 2LL * n_cu) {
+    kernel = pos ? attn_fwd64_kernel<true, E, 1, 4> : attn_fwd64_kernel<false, E, 1, 4>;
+    threads = threads_of<1>();
+  } else {
+    kernel = pos ? attn_fwd64_kernel<true, E, 2, 2> : attn_fwd64_kernel<false, E, 2, 2>;
+    threads = threads_of<2>();
+  }
+  kernel<<<grid, threads, 0, s>>>(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                  static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                                  p.B, p.T, p.Hq, p.Hkv, p.scale_log2, p.causal);
   return hipGetLastError();
 }
 

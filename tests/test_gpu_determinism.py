@@ -113,6 +113,33 @@ def test_batch_invariance(shape):
         assert torch.equal(one["lse"][0], full["lse"][b]), (b, "lse")
 
 
+def test_forward_forms_give_the_same_bits_on_peaked_scores():
+    """The 64-wide forward takes 8 waves of 32 query rows for grids of at most the
+    CU count (one workgroup per CU) or twice it (two per CU), and 4 waves of 64
+    rows beyond.  The batch sizes below put one input through all three forms;
+    q is scaled so that row maxima keep growing along the keys and blocks take
+    the slow path (redone per 32-row query block in every form).  The slices
+    must agree bitwise."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    T, Hq, Hkv = 1024, 12, 4
+    per_b = (T // 128) * Hq                       # workgroups per batch element
+    b_one = 1                                     # <= n_cu workgroups
+    b_two = max(2, n_cu // per_b + 1)             # in (n_cu, 2 n_cu]
+    b_big = 2 * n_cu // per_b + 1                 # > 2 n_cu
+    assert b_one * per_b <= n_cu < b_two * per_b <= 2 * n_cu < b_big * per_b, (n_cu, b_two, b_big)
+    w = W.custom(b_big, T, Hq, Hkv, 64, "bf16", seed=31, q_std=4.0)
+    inp = W.generate(w)
+    q, k, v, _ = to_device(inp)
+    say("forward forms", w.label(), "batches", b_one, b_two, b_big)
+    o_big, lse_big = A.fwd(q, k, v, w.scale, True)
+    for bs in (b_two, b_one):
+        o, lse = A.fwd(*(t[:bs].contiguous() for t in (q, k, v)), w.scale, True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_big[:bs]), bs
+        assert torch.equal(lse, lse_big[:bs]), bs
+    assert torch.isfinite(o_big.float()).all()
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_forward_tile_size_does_not_change_bits(D):
     """The forward picks 128-key tiles for grids of at most 512 workgroups and
