@@ -16,9 +16,8 @@
 //   * a workgroup owns 128 query rows of one (batch, query head), split between
 //     two key halves and, within each, between query groups: on grids that fit
 //     the GPU in one round (at most twice the CU count) 8 waves of 32 rows each,
-//     one workgroup per CU, or two when the grid exceeds the CU count (the kernel
-//     then held to 128 registers), so a heavy query tile's softmax (vector work a
-//     single wave issues slowly) is spread over eight waves; on larger grids 4
+//     two workgroups per CU (126 registers), so a heavy query tile's softmax
+//     (vector work a single wave issues slowly) is spread over eight waves; on larger grids 4
 //     waves of 64 rows each, two workgroups per CU, so every K/V operand read
 //     from LDS feeds two products.  A row's arithmetic is the same in every form,
 //     so all forms give the same bits;
@@ -105,9 +104,10 @@ __device__ __forceinline__ int opaque(int x) {
 constexpr int key_off(int r) { return 8 * (r >> 2) + (r & 3); }
 
 // kQB: 32-row query blocks per wave (1: 8 waves per workgroup, 2: 4 waves); kWaves:
-// waves per SIMD the kernel's registers must allow.  Each row is computed the same
-// way in every instantiation (same products, same order, its own slow path), so
-// all of them give the same bits.
+// waves per SIMD the kernel's registers must allow (4 for two 8-wave workgroups per
+// CU, 2 for two 4-wave ones).  Each row is computed the same way in every
+// instantiation (same products, same order, its own slow path), so all of them
+// give the same bits.
 template <int kQB>
 constexpr int threads_of() { return 64 * 8 / kQB; }
 template <bool kPosScale, class E, int kQB, int kWaves>
@@ -121,6 +121,11 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   const int wave = wave_id();
   const int l32 = lane & 31;
   const int g = lane >> 5;
+  // The lane index read again from the work-item id where it is needed after the
+  // loops (the empty asm keeps the compiler from holding it, or values derived
+  // from it, in registers across them): the 8-wave form then fits 128 registers
+  // without spills.  The 4-wave form has the registers and keeps them.
+  auto fresh_lane = [&]() { return kQB == 1 ? opaque((int)(threadIdx.x & 63)) : lane; };
   constexpr int QB = kQB;
   constexpr int NW = 8 / QB;       // waves per workgroup
   constexpr int NQG = NW / 2;      // query groups (32*QB rows each) per workgroup
@@ -149,12 +154,13 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   const int qw0 = qt * BM + 32 * QB * qg;  // first query row of this wave
   // Q^T as B operands: lane holds query qw0 + 32qb + l32, d = 16s + 8g + [0, 8).
   u32x4_t qf[QB][4];
-  uint32_t qoff[QB];
+  // byte offset of this lane's row of q / o (recomputed where used, to keep it out of
+  // the registers live across the loops)
+  auto row_off = [&](int qb) { return (uint32_t)(qw0 + 32 * qb + (fresh_lane() & 31)) * q_row + (uint32_t)h * 128; };
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    qoff[qb] = (uint32_t)(qw0 + 32 * qb + l32) * q_row + (uint32_t)h * 128;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[qb][s] = bload16(rq, qoff[qb] + 32 * s + 16 * g);
+    for (int s = 0; s < 4; ++s) qf[qb][s] = bload16(rq, row_off(qb) + 32 * s + 16 * g);
   }
 
   // Tile copy: instruction (tensor, group of 8 rows) with group = wave + NW*m, so a
@@ -223,8 +229,9 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   // The largest key offset a lane may see in the block at kb0 for query block qb:
   // keys up to the lane's query (causal) and below T.
   auto edge_limit = [&](int kb0, int qb) {
-    const int last = causal ? min(qw0 + 32 * qb + l32, T - 1) : T - 1;
-    return last - kb0 - 4 * g;
+    const int ln = fresh_lane();
+    const int last = causal ? min(qw0 + 32 * qb + (ln & 31), T - 1) : T - 1;
+    return last - kb0 - 4 * (ln >> 5);
   };
   // Score products of one 32-key block (tile rows krow .. +31): for every query
   // block, or (s_one) for query block qb alone.
@@ -330,19 +337,25 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   // Its P V products are issued only after this, so O stays consistent.
   auto settle_block = [&](const char* sK, int krow, int kb0, auto edge_c, u32x4_t (&p)[QB][2],
                           float (&bs)[QB]) {
+    bool any_big = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {  // each 32-row query block on its own
-      if (__any(!(bs[qb] <= kSumLimit))) {
-        u32x4_t kop[4];
-        f32x16_t acc;
-        k_operands(sK, krow, kop);
-        s_one(kop, qb, acc);
-        max_rescale_one(acc, kb0, edge_c, qb);
-        exp_one(acc, kb0, edge_c, qb, p[qb]);
-        bs[qb] = sum_one(p[qb]);
+    for (int qb = 0; qb < QB; ++qb) any_big = any_big || !(bs[qb] <= kSumLimit);
+    if (__any(any_big)) {  // rare: one branch in the common case
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {  // each 32-row query block on its own
+        if (__any(!(bs[qb] <= kSumLimit))) {
+          u32x4_t kop[4];
+          f32x16_t acc;
+          k_operands(sK, krow, kop);
+          s_one(kop, qb, acc);
+          max_rescale_one(acc, kb0, edge_c, qb);
+          exp_one(acc, kb0, edge_c, qb, p[qb]);
+          bs[qb] = sum_one(p[qb]);
+        }
       }
-      l_run[qb] += bs[qb];
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += bs[qb];
   };
 
   // One tile: blocks A (keys 32kh) and B (keys 64 + 32kh) of the tile in buffer BUF.
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   // 4(f%4) .. +3 of oacc[f/(4QB)][(f/4)%QB]; f = NF: the first and last query
   // block's m, then their l).
   constexpr int NF = 2 * QB * 4;  // float4 per lane of O^T
-  float4* part = reinterpret_cast<float4*>(smem) + qg * (NF + 1) * 64 + lane;
+  float4* part = reinterpret_cast<float4*>(smem) + qg * (NF + 1) * 64 + fresh_lane();
   if (kh == 1) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -446,11 +459,12 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
                           (oacc[db][qb][4 * j + 1] * a0 + x.y * a1) * inv);
           w[1] = E::pack2((oacc[db][qb][4 * j + 2] * a0 + x.z * a1) * inv,
                           (oacc[db][qb][4 * j + 3] * a0 + x.w * a1) * inv);
-          bstore8(ro, qoff[qb] + 2 * (32 * db + 8 * j + 4 * g), w);  // rows past T are dropped
+          bstore8(ro, row_off(qb) + 2 * (32 * db + 8 * j + 4 * (fresh_lane() >> 5)), w);  // rows past T are dropped
         }
       }
-      const int my_q = qw0 + 32 * qb + l32;
-      if (g == 0 && my_q < T) bstore_f32(rl, ((uint32_t)h * T + my_q) * 4, (m + fast_log2(l_tot)) * kLn2);
+      const int ln = fresh_lane();
+      const int my_q = qw0 + 32 * qb + (ln & 31);
+      if (ln < 32 && my_q < T) bstore_f32(rl, ((uint32_t)h * T + my_q) * 4, (m + fast_log2(l_tot)) * kLn2);
     }
   }
 }
@@ -459,8 +473,8 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
 
 const char* fwd64_tiles() {
   return "fwd64{BM=128,BN=128,grids<=2*CUs: waves=8(4 query blocks of 32 x 2 key halves),"
-         "1 workgroup/CU (grid<=CUs) else 2 (128 VGPRs); larger grids: waves=4(2 query "
-         "groups of 64 x 2 key halves),2 workgroups/CU;lds_dma_x2,mfma=32x32x16}";
+         "2 workgroups/CU; larger grids: waves=4(2 query groups of 64 x 2 key halves),"
+         "2 workgroups/CU;lds_dma_x2,mfma=32x32x16}";
 }
 
 template <class E>
@@ -473,20 +487,17 @@ hipError_t launch_fwd64_e(const Problem& p, const void* q, const void* k, const 
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipGetLastError();
-  // Every instantiation gives the same bits; the choice is speed only.  Grids that
-  // fit the GPU in one round take 8-wave workgroups of 32-row waves (one per CU with
-  // the full register file, or two per CU at 128 registers): the heavy query tiles'
-  // softmax is spread over more waves.  Larger grids take 4-wave workgroups of
-  // 64-row waves, whose K/V operands each feed two products.
+  // Both forms give the same bits; the choice is speed only.  Grids that fit the GPU
+  // in one round (two workgroups per CU, at most 128 registers) take 8-wave
+  // workgroups of 32-row waves: the heavy query tiles' softmax is spread over more
+  // waves.  Larger grids take 4-wave workgroups of 64-row waves, whose K/V operands
+  // each feed two products.
   using K = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, int,
                      int, int, int, float, int);
   const bool pos = p.scale_log2 >= 0.f;
   K kernel;
   int threads;
-  if (n_wg <= n_cu) {
-    kernel = pos ? attn_fwd64_kernel<true, E, 1, 2> : attn_fwd64_kernel<false, E, 1, 2>;
-    threads = threads_of<1>();
-  } else if (n_wg <= 2LL * n_cu) {
+  if (n_wg <= 2LL * n_cu) {
     kernel = pos ? attn_fwd64_kernel<true, E, 1, 4> : attn_fwd64_kernel<false, E, 1, 4>;
     threads = threads_of<1>();
   } else {
