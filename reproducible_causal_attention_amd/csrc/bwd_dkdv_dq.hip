@@ -19,8 +19,8 @@ constexpr int kThreads = dkdv::NTHREADS;
 static_assert(dqb::NTHREADS == kThreads, "both bodies run 512-thread workgroups");
 template <int kD>
 constexpr int smem_bytes() {
-  return dkdv::Dims<kD>::SMEM_BYTES > dqb::Dims<kD>::SMEM_BYTES ? dkdv::Dims<kD>::SMEM_BYTES
-                                                                : dqb::Dims<kD>::SMEM_BYTES;
+  return dkdv::Dims<kD>::SMEM_BYTES > dqb::Dims<kD>::SMEM2_BYTES ? dkdv::Dims<kD>::SMEM_BYTES
+                                                                 : dqb::Dims<kD>::SMEM2_BYTES;
 }
 
 // Persistent order: P workgroups (a multiple of 8, at most one per CU; workgroup
@@ -41,13 +41,19 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_dq_kernel(
     float scale, float scale_log2, int causal, int n_dq, int n_kv, int P) {
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<kD>()];
   const int x = blockIdx.x & 7, l = blockIdx.x >> 3, Q = P >> 3;
-  for (int j = 0;; ++j) {
+  auto dq_unit = [&](int j) {  // the j-th dQ unit of this workgroup; m grows with j
     const int m = 2 * Q * (j >> 1) + ((j & 1) ? 2 * Q - 1 - l : l);
-    const int u = x + 8 * m;
-    if (u >= n_dq) break;  // m grows with j
-    dqb::unit_body<E, kRope, kD>(smem, u, q, k, v, dO, lse, delta, rcos, rsin, dq, B, T, Hq, Hkv,
-                                 scale, scale_log2, causal);
+    return x + 8 * m;
+  };
+  // Unit j runs in LDS slot j % 2 and issues the copies of unit j + 1 into the
+  // other slot while it computes.
+  for (int j = 0, u = dq_unit(0); u < n_dq; ++j) {
+    const int u_next = dq_unit(j + 1);
+    dqb::unit_body<E, kRope, kD>(smem, j & 1, j > 0, u, u_next < n_dq ? u_next : -1, q, k, v, dO,
+                                 lse, delta, rcos, rsin, dq, B, T, Hq, Hkv, scale, scale_log2,
+                                 causal);
     __syncthreads();  // the next unit reuses the LDS
+    u = u_next;
   }
   for (int u = x + 8 * (Q - 1 - l); u < n_kv; u += 8 * Q) {
     dkdv::run_unit<E, kRope, kD, kSolo>(smem, u, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T, Hq,

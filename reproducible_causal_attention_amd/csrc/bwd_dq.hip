@@ -12,7 +12,7 @@ __global__ __launch_bounds__(dqb::NTHREADS) void attn_bwd_dq_kernel(
     uint16_t* __restrict__ dq, int B, int T, int Hq, int Hkv, float scale, float scale_log2,
     int causal) {
   __shared__ __attribute__((aligned(16))) char smem[dqb::Dims<kD>::SMEM_BYTES];
-  dqb::unit_body<E, false, kD>(smem, blockIdx.x, q, k, v, dO, lse, delta, nullptr, nullptr, dq, B, T,
+  dqb::unit_body<E, false, kD>(smem, 0, false, blockIdx.x, -1, q, k, v, dO, lse, delta, nullptr, nullptr, dq, B, T,
                            Hq, Hkv, scale, scale_log2, causal);
 }
 

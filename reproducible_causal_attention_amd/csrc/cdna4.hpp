@@ -300,6 +300,19 @@ __device__ __forceinline__ void dma16s(const u32x4_t& r, const void* lds, uint32
       : "memory", "m0");
 }
 
+// Load-to-LDS of one dword per lane: lane i's 4 bytes go to LDS at M0 + 4*i.
+__device__ __forceinline__ void dma4s(const u32x4_t& r, const void* lds, uint32_t off, uint32_t soff) {
+  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(lds));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds"
+      :
+      : "s"(m0), "v"(off), "s"(r), "s"(soff)
+      : "memory", "m0");
+}
+
 // Index of the calling wave within its workgroup, as a scalar (wave-uniform) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
@@ -314,6 +327,25 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 // asm wait is opaque to it: loads issued before one still count as pending).
 __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt = 0, expcnt = 7, lgkmcnt = 15 (gfx9 encoding)
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (they complete in issue order), leaving the N most recent in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt field of the immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for the wave's
+// outstanding global loads and load-to-LDS copies.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt = 0; vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
