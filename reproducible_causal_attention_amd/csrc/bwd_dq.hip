@@ -44,6 +44,6 @@ hipError_t launch_bwd_dq_f16(const Problem& p, const void* q, const void* k, con
   return launch_bwd_dq_e<F16>(p, q, k, v, dO, lse, delta, dq, s);
 }
 
-const char* bwd_dq_tiles() { return "dq_bf16{BM=128,BN=128(D=64)|64(D=128),waves=8(4 query x 2 key),mfma=32x32x16,D=64|128}"; }
+const char* bwd_dq_tiles() { return "dq_bf16{BM=128,BN=128(D=64)|64(D=128),waves=8(4 query x 2 key),mfma=32x32x16,D=64|128,D=64: rows and first tile by lds_dma into 2 slots, next unit copied during the current}"; }
 
 }  // namespace rca

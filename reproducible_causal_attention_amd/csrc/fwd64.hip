@@ -24,7 +24,8 @@
 //   * K/V tiles of 128 keys go straight from HBM into double-buffered LDS
 //     (buffer_load ... lds, no staging registers; 16-byte chunks XOR-swizzled so
 //     row reads and transposed reads are free of bank conflicts), and the per-lane
-//     LDS offsets are computed once;
+//     LDS offsets are computed once; the workgroup's Q rows arrive the same way
+//     (each row copied once, where both key halves' waves read it);
 //   * wave (query group, key half kh) takes keys 64s + 32kh .. +31 of every tile
 //     (s = 0, 1: its blocks A and B); S^T = K Q^T puts one query per lane, so a
 //     row's max and sum take one half-wave exchange, and P goes from the
@@ -145,7 +146,6 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   const uint32_t q_row = (uint32_t)Hq * 128;   // bytes between tokens of q / o
   const uint32_t kv_row = (uint32_t)Hkv * 128;  // bytes between tokens of k / v
   const size_t qe = (size_t)T * Hq * 64, ke = (size_t)T * Hkv * 64;
-  const rsrc_t rq = make_rsrc(q + b * qe, (uint32_t)T * q_row);
   const rsrc_t ro = make_rsrc(o + b * qe, (uint32_t)T * q_row);
   const rsrc_t rl = make_rsrc(lse + (size_t)b * Hq * T, (uint32_t)Hq * T * 4);
   const u32x4_t k_src = raw_rsrc(k + b * ke, (uint32_t)T * kv_row);
@@ -157,11 +157,6 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   // byte offset of this lane's row of q / o (recomputed where used, to keep it out of
   // the registers live across the loops)
   auto row_off = [&](int qb) { return (uint32_t)(qw0 + 32 * qb + (fresh_lane() & 31)) * q_row + (uint32_t)h * 128; };
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[qb][s] = bload16(rq, row_off(qb) + 32 * s + 16 * g);
-  }
 
   // Tile copy: instruction (tensor, group of 8 rows) with group = wave + NW*m, so a
   // wave's groups all have the parity of `wave` and one per-lane offset serves
@@ -213,8 +208,32 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
     }
   }
 
+  // The workgroup's 128 Q rows are copied once into K/V buffer 1 (as a tile's
+  // rows, 8 per instruction, same swizzle; rows past T read as zero) and each
+  // wave reads its B operands from there; buffer 1 is refilled only after the
+  // barrier that follows those reads.
+  {
+    const u32x4_t q_src = raw_rsrc(q + b * qe, (uint32_t)T * q_row);
+    const uint32_t q_lane = (uint32_t)r8 * q_row + (uint32_t)h * 128 +
+                            16u * (uint32_t)((lane & 7) ^ swz_of(8 * (wave & 1) + r8));
+#pragma unroll
+    for (int m = 0; m < 16 / NW; ++m) {
+      const int grp = wave + NW * m;
+      dma_rows(q_src, lds0 + (uint32_t)(BUF_BYTES + grp * 1024), q_lane, (uint32_t)(qt * BM + 8 * grp) * q_row);
+    }
+  }
   copy_tile(0, 0);  // in flight together with the Q rows
   wait_vmem();
+  __syncthreads();
+  {
+    const char* sQ = smem + BUF_BYTES + 32 * QB * qg * 128;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qf[qb][s] = *reinterpret_cast<const u32x4_t*>(sQ + 32 * qb * 128 + ka[s]);
+    }
+  }
+  lds_barrier();
 
   f32x16_t oacc[2][QB];  // O^T [db][qb]: rows d = 32db + 8*(r/4) + 4g + r%4, column = query
 #pragma unroll
@@ -223,8 +242,6 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   float m_run[QB];  // running max per query (base-2 units; an integer once set)
   float l_run[QB];        // this lane's share of the running sum
   for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -1e30f; l_run[qb] = 0.f; }
-
-  __syncthreads();
 
   // The largest key offset a lane may see in the block at kb0 for query block qb:
   // keys up to the lane's query (causal) and below T.
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
 const char* fwd64_tiles() {
   return "fwd64{BM=128,BN=128,grids<=2*CUs: waves=8(4 query blocks of 32 x 2 key halves),"
          "2 workgroups/CU; larger grids: waves=4(2 query groups of 64 x 2 key halves),"
-         "2 workgroups/CU;lds_dma_x2,mfma=32x32x16}";
+         "2 workgroups/CU;lds_dma_x2 K/V tiles,q rows by lds_dma,mfma=32x32x16}";
 }
 
 template <class E>
