@@ -52,13 +52,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_dq_kernel(
     dqb::unit_body<E, kRope, kD>(smem, j & 1, j > 0, u, u_next < n_dq ? u_next : -1, q, k, v, dO,
                                  lse, delta, rcos, rsin, dq, B, T, Hq, Hkv, scale, scale_log2,
                                  causal);
-    __syncthreads();  // the next unit reuses the LDS
+    lds_barrier();  // the next unit reuses the LDS (its own prologue waits for its copies)
     u = u_next;
   }
   for (int u = x + 8 * (Q - 1 - l); u < n_kv; u += 8 * Q) {
     dkdv::run_unit<E, kRope, kD, kSolo>(smem, u, q, k, v, dO, lse, delta, rcos, rsin, dk, dv, B, T, Hq,
                                  Hkv, scale, scale_log2, causal);
-    __syncthreads();
+    lds_barrier();
   }
 }
 

@@ -403,7 +403,7 @@ __device__ __forceinline__ void unit_body(
         }
       }
     }
-    __syncthreads();  // the regions are refilled by the next block
+    lds_barrier();  // the regions are refilled by the next block; its stores need not have landed
   }
 }
 

@@ -211,7 +211,12 @@ __device__ __forceinline__ void unit_body(
   float lse_raw, Dl;
   if constexpr (Dm::STAGED) {
     if (!staged) stage_unit<kD>(smem, slot, unit, q, k, v, dO, lse, delta, B, T, Hq, Hkv, causal);
-    wait_vmem();
+    // A staged unit's copies were issued before the previous unit's dQ stores (4 * ND
+    // per key-half-0 wave), which may stay in flight.
+    if (staged && kh == 0)
+      wait_vmem_but<4 * ND>();
+    else
+      wait_vmem();
     __syncthreads();
     const uint16_t* sQr = reinterpret_cast<const uint16_t*>(base + 2 * TILE_BYTES);
     const uint16_t* sdOr = reinterpret_cast<const uint16_t*>(base + 3 * TILE_BYTES);
