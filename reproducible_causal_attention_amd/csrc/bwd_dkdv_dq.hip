@@ -8,7 +8,9 @@
 // dK/dV launch and the last units do not start late on CUs that drew long
 // ones.  Every unit computes exactly what it computes in its own kernel (same
 // code, same order), so the results are bitwise those of the two separate
-// launches.
+// launches.  For 64-wide heads a workgroup's consecutive dQ units alternate
+// between two LDS slots, and each issues the next one's row and first-tile
+// copies while it computes, so that unit starts on data already in LDS.
 #include "dkdv_body.hpp"
 #include "dq_body.hpp"
 

@@ -70,10 +70,9 @@ struct Dims {
   static_assert(2 * ND * 4 * 64 * 16 / PASSES <= WAVE_BYTES, "a wave's parked partial must fit its region");
   static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
 };
-constexpr int SMEM_BYTES = Dims<64>::SMEM_BYTES;  // the 64-column kernels
 
 // The work of unit `unit` (a pair of key blocks of one (batch, KV head), see
-// decode_unit) for a 512-thread workgroup; smem holds SMEM_BYTES.
+// decode_unit) for a 512-thread workgroup; smem holds Dims<kD>::SMEM_BYTES.
 // kRope: q and k are the rotated q', k' (rotary embedding); the epilogue maps
 // dK back through each pair's rotation transpose with the tables rcos, rsin
 // ([T, kD/2] float32), so dk is the gradient with respect to the unrotated k.

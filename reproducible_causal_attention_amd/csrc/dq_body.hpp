@@ -69,7 +69,6 @@ struct Dims {
   static_assert(4 * (4 * ND) * 64 * 16 <= STAT_OFF, "reduction buffer must fit");
   static_assert(!STAGED || 2 * BM * kD * 2 == 2 * TILE_BYTES, "q and dO rows fill K/V buffer 1");
 };
-constexpr int SMEM_BYTES = Dims<64>::SMEM_BYTES;  // the 64-column kernels
 
 // Where unit `unit` lies: batch element b, KV head kvh, query head h, query tile
 // qt, and the number of K/V tiles its rows see.
@@ -143,7 +142,7 @@ __device__ __forceinline__ void stage_unit(char* __restrict__ smem, int slot, in
 
 // The work of unit `unit` (one 128-row query tile of one (batch, query head),
 // see decode_unit) for a 512-thread workgroup.  For 64-wide heads it runs in
-// LDS slot `slot` (smem holds SMEM_BYTES for slot 0, SMEM2_BYTES for both);
+// LDS slot `slot` (smem holds Dims<kD>::SMEM_BYTES for slot 0, SMEM2_BYTES for both);
 // `staged`: its copies were issued by stage_unit already; next >= 0: the unit
 // that follows in this workgroup, whose copies it issues into the other slot.
 // kRope: q and k are the rotated q', k' (rotary embedding); the epilogue maps
