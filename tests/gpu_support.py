@@ -2,10 +2,13 @@
 path through the C ABI, compare with the oracle, hash outputs."""
 from __future__ import annotations
 
+import contextlib
+import ctypes
 import hashlib
 import sys
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -193,3 +196,44 @@ def check_every_unit(inp: W.Inputs, gpu_np: dict, where="", n_keys: int = 32):
             for n, e in errs.items():
                 worst[n] = max(worst.get(n, 0.0), e)
     return worst
+
+
+def loaded_hip_runtime():
+    """The HIP runtime library this process already uses (torch's and the attention
+    library's), so a stream created through it is valid for both."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                return ctypes.CDLL(line.split()[-1])
+    raise RuntimeError("libamdhip64 is not loaded")
+
+
+@contextlib.contextmanager
+def cu_masked_stream(mask_kind: str):
+    """Make the current torch stream one that may use only some CUs: "first-half-cus"
+    or "first-16-cus".  Skips the test if the runtime refuses the mask."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (n_cu + 31) // 32
+    if mask_kind == "first-half-cus":
+        mask = [0xFFFFFFFF] * (words // 2) + [0] * (words - words // 2)
+    elif mask_kind == "first-16-cus":
+        mask = [0x0000FFFF] + [0] * (words - 1)
+    else:
+        raise ValueError(mask_kind)
+    hip = loaded_hip_runtime()
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    handle = ctypes.c_void_p()
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), words, (ctypes.c_uint32 * words)(*mask))
+    if rc != 0:
+        hip.hipGetErrorString.restype = ctypes.c_char_p
+        hip.hipGetLastError()  # the failed call leaves its error pending
+        pytest.skip(f"hipExtStreamCreateWithCUMask failed: {rc} {hip.hipGetErrorString(rc).decode()}")
+    try:
+        with torch.cuda.stream(torch.cuda.ExternalStream(handle.value)):
+            yield
+    finally:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        hip.hipStreamDestroy(handle)

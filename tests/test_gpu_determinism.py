@@ -4,12 +4,10 @@ prefixes.
 
 Repeated runs of one build on one device must give identical SHA-256 over the
 raw bytes of o, lse, dq, dk, dv (in that order)."""
-import ctypes
-
 import pytest
 import torch
 
-from gpu_support import run_gpu, say, sha256_outputs, to_device
+from gpu_support import cu_masked_stream, run_gpu, say, sha256_outputs, to_device
 from reproducible_causal_attention_amd import attn as A
 from reproducible_causal_attention_amd import workloads as W
 
@@ -49,48 +47,19 @@ def test_same_bits_on_another_stream_and_under_load():
     assert got_load == want
 
 
-def _loaded_hip_runtime():
-    """The HIP runtime library this process already uses (torch's and the attention
-    library's), so a stream created through it is valid for both."""
-    with open("/proc/self/maps") as f:
-        for line in f:
-            if "libamdhip64.so" in line:
-                return ctypes.CDLL(line.split()[-1])
-    raise RuntimeError("libamdhip64 is not loaded")
-
-
 @pytest.mark.parametrize("mask_kind", ["first-half-cus", "first-16-cus"])
 def test_same_bits_under_cu_masks(mask_kind):
-    """Identical bits when the stream may use only half of the CUs, or only 16.
+    """Identical bits when the stream may use only half of the CUs, or only 16 (then
+    every workgroup of the co-launched backward runs a long list of units, so each
+    dQ unit but the first starts on copies its predecessor issued).
     (A mask enabling every other CU is refused by the runtime on MI355X.)"""
     w = W.WORKLOADS["gqa-4x1024"]
     inp = W.generate(w)
     tensors = to_device(inp)
     say("CU-mask invariance", mask_kind)
     want = sha256_outputs(run_gpu(inp, tensors))
-    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    words = (n_cu + 31) // 32
-    if mask_kind == "first-half-cus":
-        mask = [0xFFFFFFFF] * (words // 2) + [0] * (words - words // 2)
-    else:
-        mask = [0x0000FFFF] + [0] * (words - 1)
-    hip = _loaded_hip_runtime()
-    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
-                                                 ctypes.POINTER(ctypes.c_uint32)]
-    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
-    handle = ctypes.c_void_p()
-    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), words, (ctypes.c_uint32 * words)(*mask))
-    if rc != 0:
-        hip.hipGetErrorString.restype = ctypes.c_char_p
-        hip.hipGetLastError()  # the failed call leaves its error pending
-        pytest.skip(f"hipExtStreamCreateWithCUMask failed: {rc} {hip.hipGetErrorString(rc).decode()}")
-    try:
-        with torch.cuda.stream(torch.cuda.ExternalStream(handle.value)):
-            got = sha256_outputs(run_gpu(inp, tensors))
-    finally:
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-        hip.hipStreamDestroy(handle)
+    with cu_masked_stream(mask_kind):
+        got = sha256_outputs(run_gpu(inp, tensors))
     assert got == want
 
 

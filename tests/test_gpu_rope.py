@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_support import TOL, as_numpy, check_against, say, to_device
+from gpu_support import TOL, as_numpy, check_against, cu_masked_stream, say, to_device
 from reproducible_causal_attention_amd import attn as A
 from reproducible_causal_attention_amd import workloads as W
 
@@ -121,6 +121,22 @@ def test_rope_is_bitwise_repeatable():
         again = run_rope(w, ts, ct, st)
         for n in first:
             assert torch.equal(first[n], again[n]), n
+
+
+def test_rope_same_bits_under_a_cu_mask():
+    """The rotary path on 16 CUs gives the bits it gives on all of them: each
+    workgroup of the co-launched backward then runs a long list of dQ units whose
+    epilogues also read the rotation tables."""
+    w = W.WORKLOADS["gqa-4x1024"]
+    inp = W.generate(w)
+    ts = to_device(inp)
+    ct, st, _, _ = tables(w.T)
+    say("rope CU-mask invariance", w.label())
+    want = run_rope(w, ts, ct, st)
+    with cu_masked_stream("first-16-cus"):
+        got = run_rope(w, ts, ct, st)
+    for n in want:
+        assert torch.equal(want[n], got[n]), n
 
 
 def round_to_dtype(x, dtype):
