@@ -157,13 +157,15 @@ class ClockSampler:
 
     def summary(self):
         """Median, min and max over the second half of the samples (the reading lags
-        the load by tens of milliseconds)."""
+        the load by tens of milliseconds); `steady` is False when the readings moved by
+        more than 10% of their maximum, in which case no single clock describes the run."""
         if not self.samples:
             return None
         import statistics
         late = self.samples[len(self.samples) // 2:]
-        return {"median_mhz": statistics.median(late), "min_mhz": min(late),
-                "max_mhz": max(late), "samples": len(late),
+        lo, hi = min(late), max(late)
+        return {"median_mhz": statistics.median(late), "min_mhz": lo,
+                "max_mhz": hi, "samples": len(late), "steady": hi - lo <= 0.1 * hi,
                 "source": "amdsmi GFX clock, sampled every ~4 ms while the step runs back "
                           "to back for --clock-seconds after the timed region (second half "
                           "of the samples)"}
@@ -612,7 +614,7 @@ def main() -> int:
         "clock": clock.summary(),
         "pct_peak_at_observed_clock": (
             round(100 * tflops / (PEAK_BF16_TFLOPS * clock.summary()["median_mhz"] / 2400.0), 2)
-            if clock.summary() else None),
+            if clock.summary() and clock.summary()["steady"] else None),
         "preprocess_gbs": round(pre_gbs, 1) if pre_gbs is not None else None,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -376,9 +376,14 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   };
 
   // One tile: blocks A (keys 32kh) and B (keys 64 + 32kh) of the tile in buffer BUF.
+  // The next tile's copies go to the other buffer, last read before the previous
+  // barrier.  The 4-wave form issues them first; the 8-wave form after block A's
+  // softmax, where the wave waits for A's row sums anyway (issued first, they held
+  // up A's score products).
+  constexpr bool kCopyFirst = NW == 4;
   auto tile = [&](int t, auto buf_c, auto edge_c) {
     constexpr int BUF = decltype(buf_c)::value;
-    copy_tile(t + 1, BUF ^ 1);  // that buffer was last read before the previous barrier
+    if (kCopyFirst) copy_tile(t + 1, BUF ^ 1);
     const char* sK = smem + BUF * BUF_BYTES;
     const char* sV = sK + TBYTES;
     const int krA = 32 * kh, krB = 64 + 32 * kh;
@@ -398,6 +403,10 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
       __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // twelve VALU
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (!kCopyFirst) {
+      copy_tile(t + 1, BUF ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     settle_block(sK, krA, kbA, edge_c, pA, bsA);
     __builtin_amdgcn_sched_barrier(0);
     // block A's P V products with block B's exponentials
