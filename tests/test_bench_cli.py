@@ -1,5 +1,5 @@
-"""bench.py's command-line contract on the host: more than one GPU is refused
-with a message, before any GPU work."""
+"""bench.py on the host: more than one GPU is refused with a message, before any
+GPU work; the clock summary flags readings that move."""
 import os
 import subprocess
 import sys
@@ -13,3 +13,19 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "single GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_clock_summary_marks_moving_readings():
+    """The clock-scaled peak is reported only for readings that stay within 10%:
+    the telemetry has been seen swinging between 1.2 and 2.3 GHz in one run."""
+    sys.path.insert(0, ROOT)
+    import bench
+    c = bench.ClockSampler.__new__(bench.ClockSampler)
+    c.samples = [2400.0] * 10 + [2300.0, 2250.0, 2300.0, 2280.0]
+    s = c.summary()
+    assert s["steady"] and s["min_mhz"] == 2250.0 and s["samples"] == 7
+    c.samples = [2339.0] * 10 + [1241.0, 2339.0, 1241.0, 1241.0]
+    s = c.summary()  # the second half: 2339 x 3, then 1241, 2339, 1241, 1241
+    assert not s["steady"] and (s["min_mhz"], s["max_mhz"], s["median_mhz"]) == (1241.0, 2339.0, 2339.0)
+    c.samples = []
+    assert c.summary() is None
