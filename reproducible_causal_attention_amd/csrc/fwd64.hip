@@ -13,14 +13,16 @@
 // softmax: one exponential per score) as matrix work, and a wave that owns only 32
 // queries re-reads every K/V row from LDS for each 32 queries, so the forward was
 // bound by LDS reads and by matrix and vector work that did not overlap.  Here:
-//   * a workgroup owns 128 query rows of one (batch, query head), split between
+//   * a workgroup owns the query rows of one (batch, query head), split between
 //     two key halves and, within each, between query groups: on grids that fit
-//     the GPU in one round (at most twice the CU count) 8 waves of 32 rows each,
-//     two workgroups per CU (126 registers), so a heavy query tile's softmax
-//     (vector work a single wave issues slowly) is spread over eight waves; on larger grids 4
-//     waves of 64 rows each, two workgroups per CU, so every K/V operand read
-//     from LDS feeds two products.  A row's arithmetic is the same in every form,
-//     so all forms give the same bits;
+//     the GPU in one round (at most twice the CU count in 128-row tiles) 8 waves
+//     of 32 rows each (128 rows), two workgroups per CU (126 registers), so a
+//     heavy query tile's softmax (vector work a single wave issues slowly) is
+//     spread over eight waves; on grids of at most half the CU count 4 waves of
+//     32 rows each (64 rows), one workgroup per CU, so no wave shares its SIMD;
+//     on larger grids 4 waves of 64 rows each (128 rows), two workgroups per CU,
+//     so every K/V operand read from LDS feeds two products.  A row's arithmetic
+//     is the same in every form, so all forms give the same bits;
 //   * K/V tiles of 128 keys go straight from HBM into double-buffered LDS
 //     (buffer_load ... lds, no staging registers; 16-byte chunks XOR-swizzled so
 //     row reads and transposed reads are free of bank conflicts), and the per-lane
@@ -53,7 +55,6 @@
 namespace rca {
 namespace {
 
-constexpr int BM = 128;                 // query rows per workgroup
 constexpr int BN = 128;                 // keys per K/V tile
 constexpr int TBYTES = BN * 128;        // one tile of one tensor: 128 rows of 128 bytes
 constexpr int BUF_BYTES = 2 * TBYTES;   // K then V
@@ -104,15 +105,15 @@ __device__ __forceinline__ int opaque(int x) {
 }
 constexpr int key_off(int r) { return 8 * (r >> 2) + (r & 3); }
 
-// kQB: 32-row query blocks per wave (1: 8 waves per workgroup, 2: 4 waves); kWaves:
-// waves per SIMD the kernel's registers must allow (4 for two 8-wave workgroups per
-// CU, 2 for two 4-wave ones).  Each row is computed the same way in every
-// instantiation (same products, same order, its own slow path), so all of them
-// give the same bits.
-template <int kQB>
-constexpr int threads_of() { return 64 * 8 / kQB; }
-template <bool kPosScale, class E, int kQB, int kWaves>
-__global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
+// kQB: 32-row query blocks per wave; kNQG: query groups per workgroup (each with
+// two waves, one per key half), so a workgroup owns 32 * kQB * kNQG query rows;
+// kWaves: waves per SIMD the kernel's registers must allow.  Each row is computed
+// the same way in every instantiation (same products, same order, its own slow
+// path), so all of them give the same bits.
+template <int kNQG>
+constexpr int threads_of() { return 128 * kNQG; }
+template <bool kPosScale, class E, int kQB, int kNQG, int kWaves>
+__global__ __launch_bounds__(threads_of<kNQG>(), kWaves) void attn_fwd64_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv,
     float scale_log2, int causal) {
@@ -128,8 +129,9 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   // without spills.  The 4-wave form has the registers and keeps them.
   auto fresh_lane = [&]() { return kQB == 1 ? opaque((int)(threadIdx.x & 63)) : lane; };
   constexpr int QB = kQB;
-  constexpr int NW = 8 / QB;       // waves per workgroup
-  constexpr int NQG = NW / 2;      // query groups (32*QB rows each) per workgroup
+  constexpr int NQG = kNQG;        // query groups (32*QB rows each) per workgroup
+  constexpr int NW = 2 * NQG;      // waves per workgroup
+  constexpr int BM = 32 * QB * NQG;  // query rows per workgroup
   const int qg = wave % NQG;       // query group: rows 32*QB*qg .. of the tile
   const int kh = wave / NQG;       // key half: blocks 32kh and 64 + 32kh of every tile
 
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
     const uint32_t q_lane = (uint32_t)r8 * q_row + (uint32_t)h * 128 +
                             16u * (uint32_t)((lane & 7) ^ swz_of(8 * (wave & 1) + r8));
 #pragma unroll
-    for (int m = 0; m < 16 / NW; ++m) {
+    for (int m = 0; m < BM / 8 / NW; ++m) {
       const int grp = wave + NW * m;
       dma_rows(q_src, lds0 + (uint32_t)(BUF_BYTES + grp * 1024), q_lane, (uint32_t)(qt * BM + 8 * grp) * q_row);
     }
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
   // barrier.  The 4-wave form issues them first; the 8-wave form after block A's
   // softmax, where the wave waits for A's row sums anyway (issued first, they held
   // up A's score products).
-  constexpr bool kCopyFirst = NW == 4;
+  constexpr bool kCopyFirst = QB == 2;
   auto tile = [&](int t, auto buf_c, auto edge_c) {
     constexpr int BUF = decltype(buf_c)::value;
     if (kCopyFirst) copy_tile(t + 1, BUF ^ 1);
@@ -498,38 +500,49 @@ __global__ __launch_bounds__(threads_of<kQB>(), kWaves) void attn_fwd64_kernel(
 }  // namespace
 
 const char* fwd64_tiles() {
-  return "fwd64{BM=128,BN=128,grids<=2*CUs: waves=8(4 query blocks of 32 x 2 key halves),"
-         "2 workgroups/CU; larger grids: waves=4(2 query groups of 64 x 2 key halves),"
+  return "fwd64{BN=128,128-row tiles<=CUs/2: BM=64,waves=4(2 query blocks of 32 x 2 key halves),"
+         "1 workgroup/CU; <=2*CUs: BM=128,waves=8(4 query blocks of 32 x 2 key halves),"
+         "2 workgroups/CU; larger grids: BM=128,waves=4(2 query groups of 64 x 2 key halves),"
          "2 workgroups/CU;lds_dma_x2 K/V tiles,q rows by lds_dma,mfma=32x32x16}";
 }
 
 template <class E>
 hipError_t launch_fwd64_e(const Problem& p, const void* q, const void* k, const void* v, void* o,
                           float* lse, hipStream_t s) {
-  const int n_qt = (p.T + BM - 1) / BM;
-  const long long n_wg = (long long)n_qt * p.B * p.Hq;
-  const dim3 grid((unsigned)n_wg);
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipGetLastError();
-  // Both forms give the same bits; the choice is speed only.  Grids that fit the GPU
-  // in one round (two workgroups per CU, at most 128 registers) take 8-wave
-  // workgroups of 32-row waves: the heavy query tiles' softmax is spread over more
-  // waves.  Larger grids take 4-wave workgroups of 64-row waves, whose K/V operands
-  // each feed two products.
+  // The forms give the same bits; the choice is speed only.  With W = the number of
+  // 128-row query tiles:
+  //  * 2W <= CUs: 4-wave workgroups of 64 rows (two query groups of 32-row waves),
+  //    one per CU, so each wave has its SIMD to itself and a heavy query tile's
+  //    chain of products and exponentials runs without a second wave beside it;
+  //  * W <= 2 * CUs (the grid fits the GPU in one round): 8-wave workgroups of 128
+  //    rows, two per CU (at most 128 registers), spreading the heavy tiles' softmax
+  //    over more waves;
+  //  * larger grids: 4-wave workgroups of 128 rows in 64-row waves, whose K/V
+  //    operands each feed two products.
   using K = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, int,
                      int, int, int, float, int);
   const bool pos = p.scale_log2 >= 0.f;
+  const long long W = (long long)((p.T + 127) / 128) * p.B * p.Hq;
   K kernel;
-  int threads;
-  if (n_wg <= 2LL * n_cu) {
-    kernel = pos ? attn_fwd64_kernel<true, E, 1, 4> : attn_fwd64_kernel<false, E, 1, 4>;
-    threads = threads_of<1>();
-  } else {
-    kernel = pos ? attn_fwd64_kernel<true, E, 2, 2> : attn_fwd64_kernel<false, E, 2, 2>;
+  int threads, rows;
+  if (2 * W <= n_cu) {
+    kernel = pos ? attn_fwd64_kernel<true, E, 1, 2, 2> : attn_fwd64_kernel<false, E, 1, 2, 2>;
     threads = threads_of<2>();
+    rows = 64;
+  } else if (W <= 2LL * n_cu) {
+    kernel = pos ? attn_fwd64_kernel<true, E, 1, 4, 4> : attn_fwd64_kernel<false, E, 1, 4, 4>;
+    threads = threads_of<4>();
+    rows = 128;
+  } else {
+    kernel = pos ? attn_fwd64_kernel<true, E, 2, 2, 2> : attn_fwd64_kernel<false, E, 2, 2, 2>;
+    threads = threads_of<2>();
+    rows = 128;
   }
+  const dim3 grid((unsigned)((long long)((p.T + rows - 1) / rows) * p.B * p.Hq));
   kernel<<<grid, threads, 0, s>>>(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                   static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
                                   p.B, p.T, p.Hq, p.Hkv, p.scale_log2, p.causal);

@@ -83,19 +83,20 @@ def test_batch_invariance(shape):
 
 
 def test_forward_forms_give_the_same_bits_on_peaked_scores():
-    """The 64-wide forward takes 8 waves of 32 query rows for grids of at most the
-    CU count (one workgroup per CU) or twice it (two per CU), and 4 waves of 64
-    rows beyond.  The batch sizes below put one input through all three forms;
-    q is scaled so that row maxima keep growing along the keys and blocks take
-    the slow path (redone per 32-row query block in every form).  The slices
-    must agree bitwise."""
+    """The 64-wide forward takes, by the number W of 128-row query tiles, 4-wave
+    workgroups of 64 rows (32-row waves, one workgroup per CU) when 2W is at most
+    the CU count, 8-wave workgroups of 128 rows (32-row waves) when W is at most
+    twice it, and 4-wave workgroups of 128 rows (64-row waves) beyond.  The batch
+    sizes below put one input through all three forms; q is scaled so that row
+    maxima keep growing along the keys and blocks take the slow path (redone per
+    32-row query block in every form).  The slices must agree bitwise."""
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     T, Hq, Hkv = 1024, 12, 4
-    per_b = (T // 128) * Hq                       # workgroups per batch element
-    b_one = 1                                     # <= n_cu workgroups
-    b_two = max(2, n_cu // per_b + 1)             # in (n_cu, 2 n_cu]
-    b_big = 2 * n_cu // per_b + 1                 # > 2 n_cu
-    assert b_one * per_b <= n_cu < b_two * per_b <= 2 * n_cu < b_big * per_b, (n_cu, b_two, b_big)
+    per_b = (T // 128) * Hq                       # 128-row tiles per batch element
+    b_one = 1                                     # 2 W <= n_cu
+    b_two = max(2, n_cu // per_b + 1)             # W in (n_cu, 2 n_cu]
+    b_big = 2 * n_cu // per_b + 1                 # W > 2 n_cu
+    assert 2 * b_one * per_b <= n_cu < b_two * per_b <= 2 * n_cu < b_big * per_b, (n_cu, b_two, b_big)
     w = W.custom(b_big, T, Hq, Hkv, 64, "bf16", seed=31, q_std=4.0)
     inp = W.generate(w)
     q, k, v, _ = to_device(inp)
