@@ -110,6 +110,31 @@ def test_forward_forms_give_the_same_bits_on_peaked_scores():
     assert torch.isfinite(o_big.float()).all()
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_forward_forms_agree_on_a_ragged_length(causal):
+    """At T = 1000 (not a multiple of the 64- or 128-row query tiles) the batch
+    sizes below take the three 64-wide forward forms (64-row workgroups for one
+    element, 8-wave workgroups of 128 rows for a few, 4-wave workgroups of 64-row
+    waves for many); every row must come out with the same bits in each, the rows
+    of the last, partial tile and the masked key blocks past each row included."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    T, Hq, Hkv = 1000, 12, 4
+    per_b = -(-T // 128) * Hq                     # 128-row tiles per batch element
+    b_two = max(2, n_cu // (2 * per_b) + 1)       # 2 W > n_cu, W <= 2 n_cu
+    b_big = 2 * n_cu // per_b + 1                 # W > 2 n_cu
+    assert 2 * per_b <= n_cu < 2 * b_two * per_b and b_two * per_b <= 2 * n_cu < b_big * per_b
+    w = W.custom(b_big, T, Hq, Hkv, 64, "bf16", seed=32, q_std=2.0, causal=causal)
+    inp = W.generate(w)
+    q, k, v, _ = to_device(inp)
+    say("forward forms, ragged", w.label(), "batches", 1, b_two, b_big)
+    o_big, lse_big = A.fwd(q, k, v, w.scale, causal)
+    for bs in (b_two, 1):
+        o, lse = A.fwd(*(t[:bs].contiguous() for t in (q, k, v)), w.scale, causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_big[:bs]), bs
+        assert torch.equal(lse, lse_big[:bs]), bs
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_forward_tile_size_does_not_change_bits(D):
     """The forward picks 128-key tiles for grids of at most 512 workgroups and
