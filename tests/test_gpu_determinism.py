@@ -47,16 +47,18 @@ def test_same_bits_on_another_stream_and_under_load():
     assert got_load == want
 
 
+@pytest.mark.parametrize("name", ["gqa-4x1024", "gqa-1x512"])
 @pytest.mark.parametrize("mask_kind", ["first-half-cus", "first-16-cus"])
-def test_same_bits_under_cu_masks(mask_kind):
+def test_same_bits_under_cu_masks(mask_kind, name):
     """Identical bits when the stream may use only half of the CUs, or only 16 (then
     every workgroup of the co-launched backward runs a long list of units, so each
-    dQ unit but the first starts on copies its predecessor issued).
+    dQ unit but the first starts on copies its predecessor issued; at 1x512 the
+    forward's one-per-CU 64-row workgroups then queue several to a CU).
     (A mask enabling every other CU is refused by the runtime on MI355X.)"""
-    w = W.WORKLOADS["gqa-4x1024"]
+    w = W.WORKLOADS[name]
     inp = W.generate(w)
     tensors = to_device(inp)
-    say("CU-mask invariance", mask_kind)
+    say("CU-mask invariance", name, mask_kind)
     want = sha256_outputs(run_gpu(inp, tensors))
     with cu_masked_stream(mask_kind):
         got = sha256_outputs(run_gpu(inp, tensors))
