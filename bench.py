@@ -63,14 +63,20 @@ def log(*a):
 
 
 def kernel_sources_digest() -> str:
-    """SHA-256 over the kernel sources (not the C-ABI validation layer): identifies
-    the kernels whose counters were taken."""
+    """SHA-256 over the kernel sources (not the C-ABI validation layer) with their
+    comments removed and white space collapsed: identifies the kernels whose
+    counters were taken, and stays the same when only a comment or the layout of
+    the text changes."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "reproducible_causal_attention_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp")) and name != "attn_api.hip":
+            text = open(os.path.join(csrc, name), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = " ".join(re.sub(r"//[^\n]*", "", text).split())
             h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+            h.update(text.encode())
     return h.hexdigest()[:16]
 
 

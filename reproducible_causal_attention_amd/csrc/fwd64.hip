@@ -125,8 +125,9 @@ __global__ __launch_bounds__(threads_of<kNQG>(), kWaves) void attn_fwd64_kernel(
   const int g = lane >> 5;
   // The lane index read again from the work-item id where it is needed after the
   // loops (the empty asm keeps the compiler from holding it, or values derived
-  // from it, in registers across them): the 8-wave form then fits 128 registers
-  // without spills.  The 4-wave form has the registers and keeps them.
+  // from it, in registers across them): with 32-row waves the 8-wave form then fits
+  // 128 registers without spills.  With 64-row waves the registers are there and
+  // the lane index stays in one.
   auto fresh_lane = [&]() { return kQB == 1 ? opaque((int)(threadIdx.x & 63)) : lane; };
   constexpr int QB = kQB;
   constexpr int NQG = kNQG;        // query groups (32*QB rows each) per workgroup
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(threads_of<kNQG>(), kWaves) void attn_fwd64_kernel(
 
   // One tile: blocks A (keys 32kh) and B (keys 64 + 32kh) of the tile in buffer BUF.
   // The next tile's copies go to the other buffer, last read before the previous
-  // barrier.  The 4-wave form issues them first; the 8-wave form after block A's
+  // barrier.  Waves of 64 rows issue them first; waves of 32 rows after block A's
   // softmax, where the wave waits for A's row sums anyway (issued first, they held
   // up A's score products).
   constexpr bool kCopyFirst = QB == 2;

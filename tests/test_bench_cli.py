@@ -29,3 +29,21 @@ def test_clock_summary_marks_moving_readings():
     assert not s["steady"] and (s["min_mhz"], s["max_mhz"], s["median_mhz"]) == (1241.0, 2339.0, 2339.0)
     c.samples = []
     assert c.summary() is None
+
+
+def test_kernel_digest_ignores_comments(tmp_path, monkeypatch):
+    """The digest that ties committed counters to the kernels they were taken on
+    changes with the code, not with a comment."""
+    import shutil
+    sys.path.insert(0, ROOT)
+    import bench
+    src = os.path.join(ROOT, "reproducible_causal_attention_amd", "csrc")
+    dst = tmp_path / "reproducible_causal_attention_amd" / "csrc"
+    shutil.copytree(src, dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    d0 = bench.kernel_sources_digest()
+    f = dst / "cdna4.hpp"
+    f.write_text(f.read_text() + "\n// a remark\n/* and a block\n   remark */\n")
+    assert bench.kernel_sources_digest() == d0
+    f.write_text(f.read_text() + "\nconstexpr int kUnused = 1;\n")
+    assert bench.kernel_sources_digest() != d0
