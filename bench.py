@@ -164,14 +164,15 @@ class ClockSampler:
     def summary(self):
         """Median, min and max over the second half of the samples (the reading lags
         the load by tens of milliseconds); `steady` is False when the readings moved by
-        more than 10% of their maximum, in which case no single clock describes the run."""
+        more than 20% of their maximum (normal DPM steps move them ~12%), in which case no
+        single clock describes the run."""
         if not self.samples:
             return None
         import statistics
         late = self.samples[len(self.samples) // 2:]
         lo, hi = min(late), max(late)
         return {"median_mhz": statistics.median(late), "min_mhz": lo,
-                "max_mhz": hi, "samples": len(late), "steady": hi - lo <= 0.1 * hi,
+                "max_mhz": hi, "samples": len(late), "steady": hi - lo <= 0.2 * hi,
                 "source": "amdsmi GFX clock, sampled every ~4 ms while the step runs back "
                           "to back for --clock-seconds after the timed region (second half "
                           "of the samples)"}
